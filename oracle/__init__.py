@@ -1,0 +1,13 @@
+"""CPU fp64 oracle (test infrastructure only; never imported by the product path)."""
+from .attention import (  # noqa: F401
+    allowed_mask,
+    attention_ref,
+    combine_ref,
+    decode_ref,
+    default_scale,
+    merge_partials,
+    probabilities_ref,
+    split_bounds,
+    split_partials_ref,
+    tiled_model,
+)
