@@ -1,0 +1,232 @@
+"""Benchmark of the attention hot path on one MI355X; prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one pass over every kernel of the path on its workload, inputs already resident in HBM:
+  * fa_fwd, bf16, causal, B=1 H=32 N=8192 d=128, scale 1/sqrt(128)   (prefill; the headline value)
+  * fa_decode, bf16, B=64 H=32 N_kv=8192 d=128, 16 splits + combine   (split-KV decode)
+  * fa_fwd, fp32, non-causal, B=1 H=1 N=256 d=64, scale 1/8            (fp32 path)
+W untimed warm-up steps, then K timed steps between device synchronisations.  Every launch is
+bracketed by HIP events on the stream it runs on, which gives each kernel's average duration over
+the timed region.  value = prefill TFLOP/s (algorithmic flops 4*d per allowed pair / kernel time);
+the decode figures (GB/s of algorithmic bytes) sit in "decode".  The CPU oracle is timed on a
+bounded sample of the prefill workload in the same run ("cpu_baseline").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+KERNEL_SOURCES = ["exact_tiled_attention_09_amd/csrc/prefill_bf16.hip", "exact_tiled_attention_09_amd/csrc/decode.hip",
+                  "exact_tiled_attention_09_amd/csrc/common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(path: str) -> str:
+    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the kernel is unchanged since."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(kernel)
+        if not rec or rec.get("source_sha") != source_sha(rec["source"]):
+            return None
+        return float(rec["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the causal prefill workload."""
+    import synthetic as syn
+    from oracle import attention_ref
+    w = syn.WORKLOADS["c3"]
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    # whole heads, one after another, until the time budget is used: every row is a full causal row
+    heads, flops, t_total = 0, 0, 0.0
+    rows = np.arange(w.Nq)
+    for h in range(w.H):
+        q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=[(0, h)]), "bf16")[None] for t in "qkv")
+        t0 = time.perf_counter()
+        attention_ref(q, k, v, w.scale, True)
+        t_total += time.perf_counter() - t0
+        flops += int(4 * w.d * (rows + 1).sum())
+        heads += 1
+        if t_total >= target_s:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads or cores,
+            "kind": "oracle",
+            "sample": f"causal bf16 prefill B1 H32 N8192 d128: {heads} of 32 heads, every row, "
+                      f"{flops / 1e9:.1f} GFLOP in fp64 in {t_total:.1f} s on {cores} host cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build runs on a single "
+              f"MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_09_amd as fa
+    import synthetic as syn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def upload(x, dtype):
+        if dtype == "f32":
+            return torch.from_numpy(x).to(dev)
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wp, wd, w1 = syn.WORKLOADS["c3"], syn.WORKLOADS["c5"], syn.WORKLOADS["c1"]
+    log(f"[bench] generating inputs: {wp.name}, {wd.name}, {w1.name}")
+    pq, pk, pv = (upload(syn.make_tensor(wp, t), "bf16") for t in "qkv")
+    po = torch.empty_like(pq)
+    plse = torch.empty(pq.shape[:-1], dtype=torch.float32, device=dev)
+    dq = upload(syn.make_tensor(wd, "q")[:, :, 0].copy(), "bf16")
+    dk = upload(syn.make_tensor(wd, "k"), "bf16")
+    dv = upload(syn.make_tensor(wd, "v"), "bf16")
+    do = torch.empty_like(dq)
+    dlse = torch.empty(dq.shape[:-1], dtype=torch.float32, device=dev)
+    S = wd.num_splits
+    ws = fa.decode_workspace(wd.B, wd.H, wd.Nkv, wd.d, S, dev)
+    fq, fk, fv = (upload(syn.make_tensor(w1, t), "f32") for t in "qkv")
+    fo = torch.empty_like(fq)
+    flse = torch.empty(fq.shape[:-1], dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(pq, pk, pv, po, plse, wp.scale, True, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_decode_split(dq, dk, dv, wd.scale, S, ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fa.fa_decode_combine(ws, do, dlse, S, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        fa.fa_fwd(fq, fk, fv, fo, flse, w1.scale, False, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = lambda a, b: np.array([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)])  # noqa: E731
+    t_prefill, t_split, t_comb, t_f32 = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
+    t_step = ms(0, 4)
+
+    pf_tflops = wp.flops / (t_prefill.mean() * 1e-3) / 1e12
+    split_bytes = 2 * wd.B * wd.H * wd.Nkv * wd.d * 2 + wd.B * wd.H * wd.d * 2   # K, V, q read once
+    split_gbs = split_bytes / (t_split.mean() * 1e-3) / 1e9
+    dec_gbs = wd.io_bytes / ((t_split.mean() + t_comb.mean()) * 1e-3) / 1e9
+    f32_tflops = w1.flops / (t_f32.mean() * 1e-3) / 1e12
+
+    rec = {
+        "metric": "prefill TFLOP/s & % bf16 MFMA peak; decode KV-read GB/s & % HBM peak",
+        "value": round(pf_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(t_step.mean()), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "fa_fwd causal bf16 prefill B1 H32 N8192 d128 (value) + fa_decode split-KV bf16 "
+                        "B64 H32 N_kv8192 d128 S16 + combine + fa_fwd fp32 B1 H1 N256 d64",
+            "prefill": {"B": wp.B, "H": wp.H, "N_q": wp.Nq, "N_kv": wp.Nkv, "d": wp.d, "causal": True,
+                        "flops_per_launch": wp.flops},
+            "decode": {"B": wd.B, "H": wd.H, "N_kv": wd.Nkv, "d": wd.d, "num_splits": S,
+                       "alg_bytes_per_call": wd.io_bytes},
+        },
+        "roofline": {
+            "kernel": "prefill_bf16_kernel<128,...,causal>",
+            "bound": "mfma",
+            "achieved": round(pf_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profiles("prefill_bf16_c3"),
+            "avg_kernel_ms": round(float(t_prefill.mean()), 4),
+            "min_kernel_ms": round(float(t_prefill.min()), 4),
+        },
+        "decode": {
+            "value": round(dec_gbs, 1),
+            "unit": "GB/s",
+            "frac_of_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "ms": round(float(t_split.mean() + t_comb.mean()), 4),
+            "roofline": {
+                "kernel": "decode_split_kernel<128>",
+                "bound": "hbm",
+                "achieved": round(split_gbs, 1),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic_from_profiles("decode_split_c5"),
+                "avg_kernel_ms": round(float(t_split.mean()), 4),
+                "combine_avg_kernel_ms": round(float(t_comb.mean()), 4),
+            },
+        },
+        "fp32_prefill": {"value": round(f32_tflops, 3), "unit": "TFLOP/s", "avg_kernel_ms": round(float(t_f32.mean()), 4)},
+        "wall_s_timed": round(wall, 4),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    del pq, pk, pv, dk, dv
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline()
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

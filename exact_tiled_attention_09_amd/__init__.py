@@ -1,0 +1,205 @@
+"""Python binding of libfa: exact tiled attention for MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of libfa.so; there is no CPU or PyTorch fallback.  PyTorch provides the
+device memory and the stream: tensors are passed by ``data_ptr()`` and work is
+enqueued on ``torch.cuda.current_stream()`` (HIP on ROCm) unless a stream is
+given.
+
+The C entry points are exposed under their C names (``fa_fwd``, ``fa_decode``,
+...), taking torch tensors instead of raw pointers; ``attention`` and ``decode``
+are allocation helpers around them.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_DEVICE = range(5)
+FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-OK status returned by libfa."""
+
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func}: {status_str(status)}: {detail}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree by build.py); raise loudly if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libfa.so is not built at {LIB_PATH}; run `python -m exact_tiled_attention_09_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i]
+    L.fa_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.fa_decode_num_splits.argtypes = [i, i, i, i, i]
+    L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.fa_decode_workspace_bytes.restype = sz
+    L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp, i]
+    L.fa_decode_split.argtypes = [vp, vp, vp, i, i, i, i, f, i, vp, sz, vp, i]
+    L.fa_decode_combine.argtypes = [vp, sz, vp, vp, i, i, i, i, vp, i]
+    L.fa_status_str.argtypes = [i]
+    L.fa_status_str.restype = ctypes.c_char_p
+    L.fa_last_error.argtypes = []
+    L.fa_last_error.restype = ctypes.c_char_p
+    L.fa_version.restype = ctypes.c_char_p
+    for name in ("fa_fwd", "fa_fwd_bf16", "fa_fwd_f32", "fa_decode", "fa_decode_split", "fa_decode_combine",
+                 "fa_decode_num_splits"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_str(s: int) -> str:
+    return lib().fa_status_str(s).decode()
+
+
+def last_error() -> str:
+    return lib().fa_last_error().decode()
+
+
+def version() -> str:
+    return lib().fa_version().decode()
+
+
+def _check(status: int, func: str):
+    if status != FA_OK:
+        raise FaError(status, func, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_tensor(name, t, shape, dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+# ----------------------------------------------------------------------------- C entry points, torch arguments
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+    """libfa fa_fwd on torch tensors: q [B,H,N_q,d], k/v [B,H,N_kv,d], o like q, lse [B,H,N_q] fp32 or None."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    _check_tensor("q", q, (B, H, Nq, d), q.dtype)
+    _check_tensor("k", k, (B, H, Nkv, d), q.dtype)
+    _check_tensor("v", v, (B, H, Nkv, d), q.dtype)
+    _check_tensor("o", o, (B, H, Nq, d), q.dtype)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H, Nq), torch.float32)
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nkv, d, float(scale), int(bool(causal)),
+                      _stream(stream), _dtype_code(q))
+    _check(st, "fa_fwd")
+
+
+def fa_decode_num_splits(B: int, H: int, N_kv: int, d: int, num_splits: int = 0) -> int:
+    return lib().fa_decode_num_splits(B, H, N_kv, d, num_splits)
+
+
+def fa_decode_workspace_bytes(B: int, H: int, N_kv: int, d: int, num_splits: int = 0) -> int:
+    return lib().fa_decode_workspace_bytes(B, H, N_kv, d, num_splits)
+
+
+def fa_decode(q, k, v, o, lse, scale: float, num_splits: int, workspace, stream=None):
+    """libfa fa_decode: q [B,H,d], k/v [B,H,N_kv,d] bf16; o [B,H,d] bf16; lse [B,H] fp32 or None;
+    workspace a byte (uint8) device tensor of at least fa_decode_workspace_bytes()."""
+    import torch
+    B, H, Nkv, d = k.shape
+    _check_tensor("q", q, (B, H, d), k.dtype)
+    _check_tensor("v", v, (B, H, Nkv, d), k.dtype)
+    _check_tensor("o", o, (B, H, d), k.dtype)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H), torch.float32)
+    st = lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nkv, d, float(scale), int(num_splits),
+                         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
+                         _dtype_code(k))
+    _check(st, "fa_decode")
+
+
+def fa_decode_split(q, k, v, scale: float, num_splits: int, workspace, stream=None):
+    B, H, Nkv, d = k.shape
+    _check_tensor("q", q, (B, H, d), k.dtype)
+    _check_tensor("v", v, (B, H, Nkv, d), k.dtype)
+    st = lib().fa_decode_split(_ptr(q), _ptr(k), _ptr(v), B, H, Nkv, d, float(scale), int(num_splits), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream), _dtype_code(k))
+    _check(st, "fa_decode_split")
+
+
+def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None):
+    import torch
+    B, H, d = o.shape
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H), torch.float32)
+    st = lib().fa_decode_combine(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(o), _ptr(lse),
+                                 B, H, d, int(num_splits), _stream(stream), _dtype_code(o))
+    _check(st, "fa_decode_combine")
+
+
+# ----------------------------------------------------------------------------- allocation helpers
+
+def attention(q, k, v, scale: float | None = None, causal: bool = False, stream=None):
+    """Allocate o and lse and run fa_fwd; returns (o, lse)."""
+    import torch
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal, stream)
+    return o, lse
+
+
+def decode_workspace(B, H, N_kv, d, num_splits=0, device="cuda"):
+    import torch
+    n = fa_decode_workspace_bytes(B, H, N_kv, d, num_splits)
+    if n == 0:
+        raise FaError(FA_ERR_INVALID_ARG, "fa_decode_workspace_bytes", last_error())
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode(q, k, v, scale: float | None = None, num_splits: int = 0, workspace=None, stream=None):
+    """Allocate o, lse (and the workspace if not given) and run fa_decode; returns (o, lse)."""
+    import torch
+    B, H, Nkv, d = k.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if workspace is None:
+        workspace = decode_workspace(B, H, Nkv, d, num_splits, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    fa_decode(q, k, v, o, lse, scale, num_splits, workspace, stream)
+    return o, lse

@@ -1,0 +1,266 @@
+// C ABI of libfa (declared in include/fa.h): argument validation and dispatch to the gfx950 kernels.
+//
+// Every check happens on the host before any HIP call, so a rejected request launches nothing and
+// leaves the outputs untouched.  Unsupported requests are errors, never a slower fallback path.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <climits>
+
+#include "fa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fa_status ok() { return FA_OK; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range span(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// n1*n2*... in 64 bits with overflow detection; false if any factor is negative or the product overflows.
+bool mul_ok(int64_t& out, std::initializer_list<int64_t> xs) {
+  int64_t r = 1;
+  for (int64_t x : xs) {
+    if (x < 0) return false;
+    if (x != 0 && r > INT64_MAX / x) return false;
+    r *= x;
+  }
+  out = r;
+  return true;
+}
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;  // per tensor; far beyond any device memory
+
+fa_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+fa_status check_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q, int N_kv,
+                    int d, float scale, int causal, fa_dtype dtype, size_t* esz) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (B < 1 || H < 1 || N_q < 1 || N_kv < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H, N_q, N_kv must be >= 1 (got %d, %d, %d, %d)", B, H, N_q, N_kv);
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head size d=%d is not built (supported: 64, 128)", d);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  if (causal && N_q > N_kv)
+    return fail(FA_ERR_INVALID_ARG, "causal attention needs N_q <= N_kv (got N_q=%d, N_kv=%d)", N_q, N_kv);
+  *esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
+  int64_t nq_el, nkv_el;
+  if (!mul_ok(nq_el, {B, H, N_q, d}) || !mul_ok(nkv_el, {B, H, N_kv, d}) || nq_el > kMaxElems || nkv_el > kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
+  const int64_t grid = dtype == FA_DTYPE_BF16 ? fa::prefill_bf16_grid(B, H, N_q, d) : fa::prefill_f32_grid(B, H, N_q, d);
+  if (grid > INT_MAX) return fail(FA_ERR_INVALID_ARG, "launch grid too large (%lld work-groups)", (long long)grid);
+  const Range rq = span(q, nq_el * *esz), rk = span(k, nkv_el * *esz), rv = span(v, nkv_el * *esz);
+  const Range ro = span(o, nq_el * *esz);
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  if (lse) {
+    const Range rl = span(lse, (size_t)B * H * N_q * 4);
+    if (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ro))
+      return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
+  }
+  return FA_OK;
+}
+
+int auto_splits(int B, int H, int N_kv) {
+  // Enough work-groups to cover 256 CUs several times, without splits shorter than 256 keys.
+  const int64_t bh = (int64_t)B * H;
+  int64_t s = (2048 + bh - 1) / bh;
+  const int64_t max_by_len = (N_kv + 255) / 256;
+  if (s > max_by_len) s = max_by_len;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+fa_status check_decode_sizes(int B, int H, int N_kv, int d, int num_splits, int* S) {
+  if (B < 1 || H < 1 || N_kv < 1) return fail(FA_ERR_INVALID_ARG, "B, H, N_kv must be >= 1");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head size d=%d is not built (supported: 64, 128)", d);
+  if (num_splits < 0 || num_splits > N_kv)
+    return fail(FA_ERR_INVALID_ARG, "num_splits must be in [0, N_kv] (got %d)", num_splits);
+  *S = num_splits == 0 ? auto_splits(B, H, N_kv) : num_splits;
+  int64_t el;
+  if (!mul_ok(el, {B, H, N_kv, d}) || el > kMaxElems) return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
+  int64_t g;
+  if (!mul_ok(g, {B, H, *S}) || g > INT_MAX) return fail(FA_ERR_INVALID_ARG, "launch grid too large");
+  return FA_OK;
+}
+
+size_t ws_bytes(int B, int H, int d, int S) { return (size_t)B * H * S * (d + 1) * sizeof(float); }
+
+fa_status check_workspace(const void* ws, size_t have, size_t need) {
+  if (!ws) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, 16)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if (have < need) return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q, int N_kv,
+                 int d, float scale, int causal, void* stream, fa_dtype dtype) {
+  size_t esz = 0;
+  const fa_status st = check_fwd(q, k, v, o, lse, B, H, N_q, N_kv, d, scale, causal, dtype, &esz);
+  if (st != FA_OK) return st;
+  fa::PrefillArgs a{q, k, v, o, lse, B, H, N_q, N_kv, d, scale, causal != 0};
+  (void)hipGetLastError();
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_prefill_bf16(a, (hipStream_t)stream)
+                                              : fa::launch_prefill_f32(a, (hipStream_t)stream);
+  return device_status(e, "fa_fwd launch");
+}
+
+fa_status fa_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
+                      int N_kv, int d, float scale, int causal, void* stream) {
+  return fa_fwd(q, k, v, o, lse, B, H, N_q, N_kv, d, scale, causal, stream, FA_DTYPE_BF16);
+}
+
+fa_status fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
+                     int N_kv, int d, float scale, int causal, void* stream) {
+  return fa_fwd(q, k, v, o, lse, B, H, N_q, N_kv, d, scale, causal, stream, FA_DTYPE_F32);
+}
+
+int fa_decode_num_splits(int B, int H, int N_kv, int d, int num_splits) {
+  int S = 0;
+  if (check_decode_sizes(B, H, N_kv, d, num_splits, &S) != FA_OK) return 0;
+  return S;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int N_kv, int d, int num_splits) {
+  int S = 0;
+  if (check_decode_sizes(B, H, N_kv, d, num_splits, &S) != FA_OK) return 0;
+  return ws_bytes(B, H, d, S);
+}
+
+fa_status fa_decode_split(const void* q, const void* k, const void* v, int B, int H, int N_kv, int d, float scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, void* stream, fa_dtype dtype) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!q || !k || !v) return fail(FA_ERR_INVALID_ARG, "q, k and v must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+  int S = 0;
+  fa_status st = check_decode_sizes(B, H, N_kv, d, num_splits, &S);
+  if (st != FA_OK) return st;
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  if (dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "decode is built for bf16 only");
+  const size_t need = ws_bytes(B, H, d, S);
+  st = check_workspace(workspace, workspace_bytes, need);
+  if (st != FA_OK) return st;
+  const size_t kv_bytes = (size_t)B * H * N_kv * d * 2, q_bytes = (size_t)B * H * d * 2;
+  const Range rw = span(workspace, need);
+  if (overlap(rw, span(q, q_bytes)) || overlap(rw, span(k, kv_bytes)) || overlap(rw, span(v, kv_bytes)))
+    return fail(FA_ERR_INVALID_ARG, "workspace overlaps an input");
+  float* ws_o = static_cast<float*>(workspace);
+  fa::DecodeArgs a{q, k, v, B, H, N_kv, d, scale, S, ws_o, ws_o + (size_t)B * H * S * d};
+  (void)hipGetLastError();
+  return device_status(fa::launch_decode_split_bf16(a, (hipStream_t)stream), "fa_decode split launch");
+}
+
+fa_status fa_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse, int B, int H, int d,
+                            int num_splits, void* stream, fa_dtype dtype) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!o) return fail(FA_ERR_INVALID_ARG, "o must be non-NULL");
+  if (!aligned(o, 16)) return fail(FA_ERR_INVALID_ARG, "o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (B < 1 || H < 1) return fail(FA_ERR_INVALID_ARG, "B, H must be >= 1");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head size d=%d is not built (supported: 64, 128)", d);
+  if (num_splits < 1) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 1 for the combine (got %d)", num_splits);
+  int64_t g;
+  if (!mul_ok(g, {B, H, num_splits, d + 1}) || g > kMaxElems) return fail(FA_ERR_INVALID_ARG, "sizes overflow");
+  if (dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "decode is built for bf16 only");
+  const size_t need = ws_bytes(B, H, d, num_splits);
+  fa_status st = check_workspace(workspace, workspace_bytes, need);
+  if (st != FA_OK) return st;
+  const Range rw = span(workspace, need), ro = span(o, (size_t)B * H * d * 2);
+  if (overlap(rw, ro)) return fail(FA_ERR_INVALID_ARG, "o overlaps the workspace");
+  if (lse) {
+    const Range rl = span(lse, (size_t)B * H * 4);
+    if (overlap(rl, rw) || overlap(rl, ro)) return fail(FA_ERR_INVALID_ARG, "lse overlaps another buffer");
+  }
+  const float* ws_o = static_cast<const float*>(workspace);
+  fa::CombineArgs a{ws_o, ws_o + (size_t)B * H * num_splits * d, o, lse, B, H, d, num_splits};
+  (void)hipGetLastError();
+  return device_status(fa::launch_decode_combine_bf16(a, (hipStream_t)stream), "fa_decode combine launch");
+}
+
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_kv, int d,
+                    float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream,
+                    fa_dtype dtype) {
+  // Validate both halves before launching either, so a rejected call enqueues nothing.
+  if (!o) return fail(FA_ERR_INVALID_ARG, "o must be non-NULL");
+  if (!aligned(o, 16)) return fail(FA_ERR_INVALID_ARG, "o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!q || !k || !v) return fail(FA_ERR_INVALID_ARG, "q, k and v must be non-NULL");
+  int S = 0;
+  fa_status st = check_decode_sizes(B, H, N_kv, d, num_splits, &S);
+  if (st != FA_OK) return st;
+  const size_t q_bytes = (size_t)B * H * d * 2, kv_bytes = (size_t)B * H * N_kv * d * 2;
+  const Range ro = span(o, q_bytes);
+  if (overlap(ro, span(q, q_bytes)) || overlap(ro, span(k, kv_bytes)) || overlap(ro, span(v, kv_bytes)))
+    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  if (lse) {
+    const Range rl = span(lse, (size_t)B * H * 4);
+    if (overlap(rl, span(q, q_bytes)) || overlap(rl, span(k, kv_bytes)) || overlap(rl, span(v, kv_bytes)) ||
+        overlap(rl, ro))
+      return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
+  }
+  if (workspace) {
+    const Range rw = span(workspace, ws_bytes(B, H, d, S));
+    if (overlap(rw, ro) || (lse && overlap(rw, span(lse, (size_t)B * H * 4))))
+      return fail(FA_ERR_INVALID_ARG, "workspace overlaps an output");
+  }
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  if (dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "decode is built for bf16 only");
+  st = check_workspace(workspace, workspace_bytes, ws_bytes(B, H, d, S));
+  if (st != FA_OK) return st;
+  st = fa_decode_split(q, k, v, B, H, N_kv, d, scale, S, workspace, workspace_bytes, stream, dtype);
+  if (st != FA_OK) return st;
+  return fa_decode_combine(workspace, workspace_bytes, o, lse, B, H, d, S, stream, dtype);
+}
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_DEVICE: return "FA_ERR_DEVICE";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+const char* fa_version(void) { return "libfa 0.1 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Host-side launchers of the gfx950 attention kernels (internal to libfa; the C ABI lives in fa_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Nq, Nkv, d;
+  float scale;
+  bool causal;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int B, H, Nkv, d;
+  float scale;
+  int splits;
+  float* ws_o;    // [B,H,S,d]
+  float* ws_lse;  // [B,H,S]
+};
+
+struct CombineArgs {
+  const float* ws_o;
+  const float* ws_lse;
+  void* o;
+  float* lse;
+  int B, H, d, splits;
+};
+
+// Each launcher assumes validated arguments and returns the launch status.
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode_split_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_combine_bf16(const CombineArgs& a, hipStream_t s);
+
+// Grid-size helpers shared with argument validation.
+int64_t prefill_bf16_grid(int B, int H, int Nq, int d);
+int64_t prefill_f32_grid(int B, int H, int Nq, int d);
+
+}  // namespace fa

@@ -1,0 +1,139 @@
+/*
+ * fa.h -- C ABI of libfa: exact tiled scaled-dot-product attention on MI355X (gfx950).
+ *
+ * The operation is Attention(Q,K,V) = softmax(scale * Q K^T) V, the equation of
+ * "FlashAttention Explained: How AI Models Process Attention Faster and Use Less
+ * Memory", section "Understanding Attention in Transformer Models" (there
+ * scale = 1/sqrt(d_k)).  It is computed in Q/K/V tiles with a running row
+ * maximum, a running denominator and a rescaled partial output (same page, "How
+ * FlashAttention Works", parts 1 and 3; "Flash Attention Explained: Same Maths,
+ * Far Less Memory", section "The idea: never materialise the matrix"), so the
+ * N_q x N_kv score matrix is never written to device memory and is not an output.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout     Contiguous row-major [B, H, N, d] with d innermost, for q, k, v and o.
+ *             lse is float32 [B, H, N_q]: the natural-log log-sum-exp of each row,
+ *             ln sum_{allowed j} exp(scale * q_i . k_j), scale included.
+ *  Pointers   Device pointers (or any pointer the device can read/write), q/k/v/o
+ *             and workspaces 16-byte aligned, lse 4-byte aligned.  Outputs must
+ *             not overlap inputs.  lse may be NULL (then it is not written).
+ *  Mask       causal != 0 allows key j for query i iff j <= i + (N_kv - N_q)
+ *             (bottom-right alignment; equal to the lower triangle when N_q == N_kv).
+ *             It requires N_q <= N_kv so that every row has at least one key.
+ *  Domain     d in {64, 128}; B, H, N_q, N_kv >= 1; scale finite (0 and negative
+ *             allowed); B*H*N*d*elem_size and the launch grid must fit the device
+ *             limits.  Anything else is an error code -- never a silent slower path.
+ *  Ownership  The caller owns every buffer, including workspaces.  The library
+ *             never allocates, frees or synchronises, and never changes the current
+ *             device.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *             stream of the current device) and the call returns; outputs are valid
+ *             once the caller has synchronised that stream.  Inputs are read-only.
+ *  Errors     Every argument is validated on the host before anything is launched;
+ *             on a non-OK status nothing was enqueued and the outputs are untouched.
+ *             A launch failure returns FA_ERR_DEVICE.  fa_last_error() gives a
+ *             thread-local description of the last non-OK status.  No exception or
+ *             abort crosses this boundary.
+ *  Threads    Re-entrant; the only global state is the thread-local error text.
+ *  Results    Bitwise deterministic run to run for the same arguments.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* NULL/misaligned/overlapping pointer, size < 1, causal with N_q > N_kv, ... */
+  FA_ERR_UNSUPPORTED = 2, /* valid request outside the built domain (head size, dtype) */
+  FA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than fa_decode_workspace_bytes() */
+  FA_ERR_DEVICE = 4       /* the HIP runtime refused a launch */
+} fa_status;
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 } fa_dtype;
+
+/*
+ * fa_fwd -- attention forward for N_q queries against N_kv keys per (batch, head).
+ *
+ * q [B,H,N_q,d], k [B,H,N_kv,d], v [B,H,N_kv,d] in `dtype`; writes o [B,H,N_q,d] in
+ * `dtype` and, if lse != NULL, lse [B,H,N_q] float32.
+ * bf16: scores and value sums accumulate in fp32 on the matrix cores, the
+ * softmax runs in fp32, the probabilities enter the value product as bf16 and
+ * o is rounded to bf16 to nearest-even.  f32: fp32 throughout.
+ * Passage: the attention equation and "How FlashAttention Works" of the page
+ * named at the top; prefill is "Where you actually feel it" of "Flash Attention
+ * Explained: Same Maths, Far Less Memory".
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
+                 int N_kv, int d, float scale, int causal, void* stream, fa_dtype dtype);
+
+/* fa_fwd with the element type fixed (bf16 / f32); arguments as for fa_fwd. */
+fa_status fa_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
+                      int N_kv, int d, float scale, int causal, void* stream);
+fa_status fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
+                     int N_kv, int d, float scale, int causal, void* stream);
+
+/*
+ * Split-KV decode: one query per sequence against its cached keys and values,
+ * no mask ("Flash Attention Explained: Same Maths, Far Less Memory", section
+ * "Where you actually feel it": during decode the score matrix is a single row).
+ *
+ * The N_kv keys are cut into S contiguous ranges; split s covers keys
+ * [s*c, min((s+1)*c, N_kv)) with c = ceil(N_kv / S) (a range may be empty).  The
+ * split kernel writes, per (b, h, s), the normalised partial output O_s and its
+ * log-sum-exp lse_s (lse_s = -inf and O_s = 0 for an empty range) into the
+ * workspace; the combine kernel merges them:
+ *   M = max_s lse_s,  w_s = exp(lse_s - M),  o = sum_s w_s O_s / sum_s w_s,
+ *   lse = M + ln sum_s w_s.
+ *
+ * Workspace layout (caller-owned, 16-byte aligned, fa_decode_workspace_bytes()):
+ *   float O_s  [B, H, S, d]      at byte offset 0
+ *   float lse_s[B, H, S]         at byte offset B*H*S*d*4
+ */
+
+/* The split count fa_decode uses for num_splits == 0 (auto); >= 1. Returns 0 on invalid sizes. */
+int fa_decode_num_splits(int B, int H, int N_kv, int d, int num_splits);
+
+/* Workspace bytes fa_decode needs for these sizes (num_splits 0 = auto). Returns 0 on invalid sizes. */
+size_t fa_decode_workspace_bytes(int B, int H, int N_kv, int d, int num_splits);
+
+/*
+ * fa_decode -- q [B,H,d], k [B,H,N_kv,d], v [B,H,N_kv,d] (bf16); writes o [B,H,d] (bf16,
+ * rounded to nearest-even) and, if lse != NULL, lse [B,H] float32.
+ * num_splits in [0, N_kv] (0 = auto).  The workspace holds the partials afterwards.
+ * dtype must be FA_DTYPE_BF16 (FA_DTYPE_F32 returns FA_ERR_UNSUPPORTED).
+ */
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_kv,
+                    int d, float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream,
+                    fa_dtype dtype);
+
+/*
+ * The two halves of fa_decode, for callers that time or reuse them separately.
+ * fa_decode_split writes only the workspace partials; fa_decode_combine reads
+ * partials laid out as above (S = num_splits, which must be >= 1 here) and writes
+ * o (bf16) and lse.  The combine is also the merge a caller needs when the key
+ * ranges of one row were processed elsewhere.
+ */
+fa_status fa_decode_split(const void* q, const void* k, const void* v, int B, int H, int N_kv, int d, float scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, void* stream, fa_dtype dtype);
+fa_status fa_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse, int B, int H,
+                            int d, int num_splits, void* stream, fa_dtype dtype);
+
+/* Human-readable name of a status code (static storage). */
+const char* fa_status_str(fa_status s);
+
+/* Thread-local text describing the last non-OK status returned on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* Library version string, e.g. "libfa 0.1 gfx950". */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

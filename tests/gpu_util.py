@@ -1,0 +1,36 @@
+"""Helpers for the GPU tests: move seeded host inputs to the device and results back (plumbing only)."""
+import numpy as np
+
+import synthetic as syn
+
+TOL_O = {"f32": 2e-5, "bf16": 1.6e-2}
+TOL_LSE = 1e-3
+
+
+def to_dev(arr: np.ndarray, dtype: str):
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_host64(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def inputs(w: syn.Workload):
+    """Host storage arrays (f32 or bf16 bits) for q, k, v and their exact float64 values."""
+    host = {t: syn.make_tensor(w, t) for t in ("q", "k", "v")}
+    f64 = {t: syn.as_f64(host[t], w.dtype) for t in host}
+    return host, f64
+
+
+def max_err(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(a)):
+        return float("inf")
+    return float(np.abs(a - b).max())
