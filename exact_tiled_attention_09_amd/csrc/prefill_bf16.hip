@@ -1,30 +1,38 @@
 // Tiled exact attention forward, bf16 in / bf16 out, fp32 accumulation, for gfx950 (MI355X).
 //
-// Method: the Q/K/V tiling with a running row maximum m, a running denominator l and a rescaled
-// partial output O ("FlashAttention Explained: How AI Models Process Attention Faster and Use Less
-// Memory", "How FlashAttention Works", parts 1-3; "Flash Attention Explained: Same Maths, Far Less
-// Memory", "The idea: never materialise the matrix").  Per key tile j and query row i:
-//   m_new = max(m, max_j s_ij * c),  alpha = 2^(m - m_new),  p_ij = 2^(s_ij * c - m_new),
-//   l = alpha * l + sum_j p_ij,      O = alpha * O + sum_j p_ij v_j,
-// with c = |scale| * log2(e) (exp2 with log2(e) folded into the scale is the same exponential); at
-// the end O / l and LSE = ln2 * (m + log2 l).  The score tile lives only in registers.
+// Method: Q/K/V tiling with a running row maximum m, a running denominator l and a rescaled partial
+// output O ("FlashAttention Explained: How AI Models Process Attention Faster and Use Less Memory",
+// "How FlashAttention Works", parts 1-3; "Flash Attention Explained: Same Maths, Far Less Memory",
+// "The idea: never materialise the matrix").  For each tile of keys and each query row i:
+//   x_ij = s_ij * c  (c = |scale| * log2 e: exp2 with log2 e folded into the scale is the same exp)
+//   m' = max(m, max_j x_ij),  p_ij = 2^(x_ij - m'),  l = 2^(m - m') l + sum_j p_ij,
+//   O = 2^(m - m') O + sum_j p_ij v_j;   at the end O / l and LSE = ln2 * (m + log2 l).
+// The running maximum is moved only when a tile's maximum exceeds it by more than kTau (log2 units),
+// so every exponent stays <= kTau and O, l need rescaling only on those rare moves; O / l and LSE do
+// not depend on which reference maximum is used.  O is normalised by the sum of the same bf16
+// weights that entered the value product (so a dominant weight cancels exactly), the LSE by the fp32
+// sum.  The score tile lives only in registers.
 //
-// gfx950 mapping (one work-group per (batch*head, query tile), NW waves, NB*32 query rows per wave):
-//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K is the A operand
-//    (read from LDS), Q^T the B operand (held in VGPRs for the whole kernel).  In the 32x32 result
-//    a lane holds one query column and 16 keys, so lane l and lane l^32 together own query l%32:
-//    row max / row sum are in-lane reductions plus one exchange with lane l^32.
-//  * O^T = V^T P^T on the same instruction: P^T is the B operand taken straight from the lane's own
-//    score registers (keys are contracted in the order the score layout gives them), V^T the A
-//    operand, read from an LDS copy of V stored transposed with the matching key order.  The
-//    transpose happens while staging: each thread loads a 4-key x 8-d block (four 16-byte global
-//    loads) and writes eight 8-byte LDS rows after v_perm_b32 byte shuffles.
-//  * K and V^T tiles are double-buffered in LDS (the next tile's global loads are in flight while
-//    the current tile is computed); 16-byte LDS chunks are XOR-swizzled per row against bank conflicts.
-//  * Causal tiles above the diagonal are never loaded; a wave skips the math of a tile that is fully
-//    masked for its rows; only diagonal and ragged-tail tiles evaluate the mask.
+// gfx950 mapping: one work-group of 4 waves per (batch*head, 128-query tile), 32 query rows per wave,
+// two work-groups per CU (two waves per SIMD: one wave's softmax runs while the other's MFMAs run).
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS = A operand, Q^T in VGPRs = B operand): in
+//    the 32x32 result a lane holds one query and 16 keys; lanes l and l^32 together hold the row, so
+//    row max / row sum are in-lane reductions plus one v_permlane32_swap.
+//  * O^T = V^T P^T on the same instruction: P^T (B operand) is the lane's own score registers
+//    rounded to bf16, keys contracted in the order the score layout gives them; V^T (A operand) is
+//    read from row-major V in LDS with ds_read_b64_tr_b16, whose 16-lane transpose delivers 4 keys at
+//    one d per lane, in exactly that key order.
+//  * K and V tiles of 64 keys go global -> LDS with direct 16-byte loads (global_load_lds_dwordx4, no
+//    staging registers), double-buffered with one barrier per tile: tile t+1 is in flight while tile t
+//    is computed.  16-byte chunks are XOR-swizzled within each row (the swizzle is applied through
+//    each lane's source address) so every fragment read hits distinct banks, and fragment addresses
+//    are per-lane bases plus compile-time offsets.
+//  * Causal tiles above the diagonal are never loaded; a wave skips the math of tiles that lie fully
+//    above its rows; only diagonal and ragged-tail tiles evaluate the mask.
 //  * Work-group ids are remapped so each XCD walks contiguous (head, tile) ranges, heaviest causal
-//    tiles first.
+//    query tiles first.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -37,40 +45,77 @@ struct PrefillParams {
   uint16_t* __restrict__ o;
   float* __restrict__ lse;
   int Nq, Nkv, off, n_qt, total;
-  float c;        // |scale| * log2(e)
-  uint32_t qxor;  // 0x80008000 when scale < 0: q is negated on load (exact) so that c >= 0
+  float c;        // max(|scale| * log2(e), 2^-126): strictly positive so masked -inf scores give 2^-inf = 0
+  uint32_t qxor;  // 0x80008000 when scale < 0: q is negated on load (exact) so that c > 0
 };
 
-template <int D, int NB, int NW, int BC>
-struct Bf16Cfg {
-  static constexpr int BR = NW * NB * 32;  // query rows per work-group
-  static constexpr int NT = NW * 64;       // threads
-  static constexpr int KCH = D / 8;        // 16-byte chunks per K row
-  static constexpr int VCH = BC / 8;       // 16-byte chunks per V^T row
-  static constexpr int KCPT = BC * KCH / NT;   // K chunks staged per thread
-  static constexpr int KPT = BC * D / (8 * NT);  // keys per thread in the V staging (4 or 2)
-  static constexpr int MB = BC / 32;       // 32-key blocks per tile
-  static constexpr int KS = D / 16;        // MFMA k-steps over d
-  static constexpr int MBD = D / 32;       // 32-wide d blocks
-  static constexpr int KC = BC / 16;       // 16-key chunks contracted by one PV MFMA
-  static constexpr int LDS_K = BC * D;     // bf16 elements per stage
-  static constexpr int LDS_V = D * BC;
-  static constexpr int LDS_ELEMS = 2 * (LDS_K + LDS_V);
-  static_assert(KPT == 2 || KPT == 4, "V staging handles 2 or 4 keys per thread");
-  static_assert(BC * KCH % NT == 0, "K staging must divide evenly");
-  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shapes");
-};
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units (p <= 2^8)
 
-// XOR swizzles of the 16-byte chunk index within a row (see the bank analysis in the design notes).
 template <int D>
-__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-template <int BC>
-__device__ __forceinline__ int swz_v(int d) { return BC == 128 ? (d & 15) : ((d >> 1) & 7); }
+struct Cfg {
+  static constexpr int NW = 4;             // waves per work-group
+  static constexpr int NT = NW * 64;       // threads
+  static constexpr int BR = NW * 32;       // query rows per work-group (32 per wave)
+  static constexpr int BC = 64;            // keys per tile
+  static constexpr int ROWB = 2 * D;       // bytes per K / V row
+  static constexpr int CH = D / 8;         // 16-byte chunks per row
+  static constexpr int TILEB = BC * ROWB;  // bytes per K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB; // K tile then V tile
+  static constexpr int NSTAGE = 2;
+  static constexpr int LPT = TILEB / (NT * 16);  // 16-byte direct loads per thread per tile (each of K, V)
+  static constexpr int RPL = 1024 / ROWB;  // rows covered by one wave-wide 1 KB load
+  static constexpr int KS = D / 16;        // MFMA k-steps over d
+  static constexpr int MBD = D / 32;       // 32-wide d blocks of O^T
+  static_assert(TILEB % (NT * 16) == 0, "tile loads must divide evenly");
+  static_assert(NSTAGE * STAGEB <= 65536, "fragment reads use 16-bit immediate offsets");
+};
 
-template <int D, int NB, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams p) {
-  using C = Bf16Cfg<D, NB, NW, BC>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+// 16-byte-chunk XOR swizzles within a row, chosen so that the fragment reads below hit distinct banks:
+//  K (16 lanes read 16 rows at one logical chunk): spread the rows over all chunk positions;
+//  V (ds_read_b64_tr_b16: 32 lanes read 4 rows x 4 chunks): spread the 4 rows by chunk xor 4k.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// One wave-wide direct global -> LDS load of 16 bytes per lane into lds_block + 16 * lane.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+// max / sum of x over lanes l and l^32 (v_permlane32_swap exchanges the two half-waves).
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// acc + sum of the 8 bf16 values of a fragment (v_dot2_f32_bf16 against ones).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pp = {p[2 * i], p[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pp, one, acc, false);
+  }
+  return acc;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NSTAGE * C::STAGEB];
 
   const int lid = xcd_logical_id(blockIdx.x, p.total);
   const int bh = lid / p.n_qt;
@@ -84,226 +129,199 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillParams p) 
   const uint16_t* __restrict__ qg = p.q + head_q;
   const uint16_t* __restrict__ kg = p.k + head_kv;
   const uint16_t* __restrict__ vg = p.v + head_kv;
-  const int qw0 = q0 + w * NB * 32;  // first query row of this wave
+  const int qw0 = q0 + w * 32;  // first query row of this wave
+  const int qi = qw0 + l32;     // this lane's query row
+  const float c = p.c;
 
-  // Q^T fragments: lane holds query qw0 + nb*32 + l32, d = ks*16 + 8h .. +7.
-  bf16x8 qf[NB][C::KS];
+  // Q^T fragments: lane holds query qi, d = ks*16 + 8h .. +7.
+  bf16x8 qf[C::KS];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int qi = qw0 + nb * 32 + l32;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qi < p.Nq) x = load16(qg + (size_t)qi * D + ks * 16 + 8 * h);
-      x ^= p.qxor;
-      qf[nb][ks] = __builtin_bit_cast(bf16x8, x);
-    }
+  for (int ks = 0; ks < C::KS; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qi < p.Nq) x = load16(qg + (size_t)qi * D + ks * 16 + 8 * h);
+    x ^= p.qxor;
+    qf[ks] = __builtin_bit_cast(bf16x8, x);
   }
 
   int kv_end = p.Nkv;
   if (CAUSAL) kv_end = min(p.Nkv, q0 + C::BR + p.off);
-  const int n_tiles = (kv_end + BC - 1) / BC;
-  const int wave_kv_end = CAUSAL ? min(p.Nkv, qw0 + NB * 32 + p.off) : p.Nkv;
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  // keys this wave needs (0 when the wave's rows lie past N_q)
+  const int wave_kv_end = qw0 >= p.Nq ? 0 : (CAUSAL ? min(p.Nkv, qw0 + 32 + p.off) : p.Nkv);
+  const int lim = CAUSAL ? min(p.Nkv - 1, qi + p.off) : p.Nkv - 1;  // last key this row may attend
 
-  f32x16 oacc[NB][C::MBD];
-  float m_run[NB], l_run[NB];
+  f32x16 oacc[C::MBD];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_run[nb] = kNegInf;
-    l_run[nb] = 0.f;
+  for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[mbd] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f, lh_run = 0.f;
+
+  // ---------------------------------------------------------------- global -> LDS (direct, no registers)
+  // Load i of wave w fills the 1 KB block (w * LPT + i) of a tile: rows RPL*(w*LPT+i) + lane/CH, physical
+  // chunk lane%CH, which holds logical chunk (lane%CH) ^ swizzle(row).  Rows past N_kv re-read the last
+  // row (finite values; their scores are masked, so they carry zero weight).
+  int ld_row[C::LPT], ld_ck[C::LPT], ld_cv[C::LPT];
 #pragma unroll
-    for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[nb][mbd] = f32x16{};
+  for (int i = 0; i < C::LPT; ++i) {
+    const int r = C::RPL * (w * C::LPT + i) + lane / C::CH, pc = lane % C::CH;
+    ld_row[i] = r;
+    ld_ck[i] = (pc ^ swz_k<D>(r)) * 8;
+    ld_cv[i] = (pc ^ swz_v<D>(r)) * 8;
+  }
+  auto load_tile = [&](int t, int stage) {
+    const int kv0 = t * C::BC;
+    uint8_t* st = smem + stage * C::STAGEB;
+#pragma unroll
+    for (int i = 0; i < C::LPT; ++i) {
+      const size_t row = (size_t)min(kv0 + ld_row[i], p.Nkv - 1) * D;
+      uint8_t* blk = st + 1024 * (w * C::LPT + i);
+      load_lds16(kg + row + ld_ck[i], blk);
+      load_lds16(vg + row + ld_cv[i], blk + C::TILEB);
+    }
+  };
+
+  // ---------------------------------------------------------------- fragment addresses (bytes)
+  // K (A operand of S^T): row 32*mb + l32, logical chunk 2ks + h.
+  int k_off[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_k<D>(l32));
+  // V^T (A operand of O^T) through ds_read_b64_tr_b16: in lane group G = lane/16 (h = G/2, dh = G%2),
+  // lane j points at row key0 + j/4, d = 32*mbd + 16*dh + 4*(j%4); lane i then receives
+  // V[key0 + t][32*mbd + 16*dh + i], t = 0..3, with key0 = 16*kc + 8*u + 4*h.  The swizzle of those
+  // rows only depends on j/4, so each mbd has one per-lane base and (kc, u) are immediate offsets.
+  const int tr_j = lane & 15, tr_dh = (lane >> 4) & 1, tr_row = 4 * h + tr_j / 4;
+  int v_off[C::MBD];
+#pragma unroll
+  for (int mbd = 0; mbd < C::MBD; ++mbd) {
+    const int d0 = 32 * mbd + 16 * tr_dh + 4 * (tr_j & 3);
+    v_off[mbd] = C::TILEB + tr_row * C::ROWB + 16 * ((d0 >> 3) ^ swz_v<D>(tr_row)) + 2 * (d0 & 7);
   }
 
-  u32x4 kst[C::KCPT];
-  u32x4 vst[C::KPT];
-  const int v_cd = tid % (D / 8), v_g = tid / (D / 8);
-
-  auto load_tile = [&](int t) {
-    const int kv0 = t * BC;
+  // ---------------------------------------------------------------- one tile
+  auto compute_tile = [&](auto stage_tag, auto masked_tag, int kv0) {
+    constexpr int STAGE = decltype(stage_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const uint8_t* sb = smem + STAGE * C::STAGEB;
+    // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks)
+    f32x16 S[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int i = 0; i < C::KCPT; ++i) {
-      const int x = tid + i * C::NT, row = x / C::KCH, c = x % C::KCH, key = kv0 + row;
-      kst[i] = key < p.Nkv ? load16(kg + (size_t)key * D + c * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-    for (int e = 0; e < C::KPT; ++e) {
-      const int key = kv0 + v_g * C::KPT + e;
-      vst[e] = key < p.Nkv ? load16(vg + (size_t)key * D + v_cd * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    uint16_t* ks = smem + stage * (C::LDS_K + C::LDS_V);
-    uint16_t* vs = ks + C::LDS_K;
-#pragma unroll
-    for (int i = 0; i < C::KCPT; ++i) {
-      const int x = tid + i * C::NT, row = x / C::KCH, c = x % C::KCH;
-      store16(ks + (row * C::KCH + (c ^ swz_k<D>(row))) * 8, kst[i]);
-    }
-    // V^T: keys of each 16-key chunk are stored in the order the score layout contracts them,
-    // [0-3, 8-11, 4-7, 12-15], so lane half h later reads its 8 keys as one 16-byte chunk.
-    const int kb = v_g * C::KPT;
-    const int kc = kb >> 4, e = kb & 15, lg = e >> 2;
-    const int cc = 2 * kc + (lg & 1), elem = 4 * (lg >> 1) + (e & 3);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int dd = 0; dd < 2; ++dd) {
-        const int d = v_cd * 8 + 2 * j + dd;
-        uint16_t* dst = vs + d * BC + (cc ^ swz_v<BC>(d)) * 8 + elem;
-        if constexpr (C::KPT == 4) {
-          u32x2 val;
-          val[0] = dd ? perm_hi(vst[1][j], vst[0][j]) : perm_lo(vst[1][j], vst[0][j]);
-          val[1] = dd ? perm_hi(vst[3][j], vst[2][j]) : perm_lo(vst[3][j], vst[2][j]);
-          *reinterpret_cast<u32x2*>(dst) = val;
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = dd ? perm_hi(vst[1][j], vst[0][j]) : perm_lo(vst[1][j], vst[0][j]);
-        }
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + k_off[ks] + mb * 32 * C::ROWB);
+        S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
       }
     }
-  };
-
-  auto compute_tile = [&](int kv0, int stage) {
-    const uint16_t* ks = smem + stage * (C::LDS_K + C::LDS_V);
-    const uint16_t* vs = ks + C::LDS_K;
-    f32x16 sacc[C::MB][NB];
+    // mask (diagonal and ragged-tail tiles only)
+    if constexpr (MASKED) {
+      const int rel = lim - kv0 - 4 * h;  // key offset within the tile allowed iff 8*(r/4) + (r%4) + 32*mb <= rel
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sacc[mb][nb] = f32x16{};
-    // S^T = K Q^T
-#pragma unroll
-    for (int kstep = 0; kstep < C::KS; ++kstep) {
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        const int row = mb * 32 + l32, c = 2 * kstep + h;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (row * C::KCH + (c ^ swz_k<D>(row))) * 8);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][kstep], sacc[mb][nb], 0, 0, 0);
-      }
+        for (int r = 0; r < 16; ++r)
+          if (32 * mb + 8 * (r >> 2) + (r & 3) > rel) S[mb][r] = kNegInf;
     }
-    // mask (diagonal and ragged tail only), online softmax
-    const bool need_mask = (kv0 + BC > p.Nkv) || (CAUSAL && kv0 + BC - 1 > qw0 + p.off);
+    // online softmax with the lazy reference maximum
+    float mx = S[0][0];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if (need_mask) {
-        const int qi = qw0 + nb * 32 + l32;
-        const int lim = CAUSAL ? min(p.Nkv - 1, qi + p.off) : p.Nkv - 1;  // last allowed key
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[0][r]);
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[1][r]);
+    mx = pair_max(mx);
+    const float mt = mx * c;
+    const bool up = mt > m_run + kTau;
+    const float mn = up ? mt : m_run;
+    const float alpha = up ? exp2_hw(m_run - mn) : 1.f;
+    m_run = mn;
+    float rs = 0.f, rsh = 0.f;
+    bf16x8 P[4];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > lim) sacc[mb][nb][r] = kNegInf;
-          }
+    for (int kc = 0; kc < 4; ++kc) {
+      float pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pr[i] = exp2_hw(fmaf(S[kc >> 1][8 * (kc & 1) + i], c, -mn));
+        rs += pr[i];
       }
-      float mx = kNegInf;
+      u32x4 pk;
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
+      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+      P[kc] = __builtin_bit_cast(bf16x8, pk);
+      rsh = sum_bf16x8(P[kc], rsh);
+    }
+    l_run = alpha * l_run + rs;
+    lh_run = alpha * lh_run + rsh;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][nb][r]);
-      mx = fmaxf(mx, xor32(mx));
-      const float mt = (mx == kNegInf) ? kNegInf : mx * p.c;
-      const float mn = fmaxf(m_run[nb], mt);
-      const float alpha = (m_run[nb] == kNegInf) ? 0.f : exp2_hw(m_run[nb] - mn);
-      const float msub = (mn == kNegInf) ? 0.f : mn;
-      float rs = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float s = sacc[mb][nb][r];
-          float pv = exp2_hw(fmaf(s, p.c, -msub));
-          if (need_mask) pv = (s == kNegInf) ? 0.f : pv;
-          rs += pv;
-          sacc[mb][nb][r] = pv;
-        }
-      l_run[nb] = alpha * l_run[nb] + rs;
-      m_run[nb] = mn;
-#pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[nb][mbd] *= alpha;
+      for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[mbd] *= alpha;
     }
     // O^T += V^T P^T
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-      bf16x8 pf[NB];
+    for (int mbd = 0; mbd < C::MBD; ++mbd) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const f32x16& s = sacc[kc >> 1][nb];
-        const int r0 = 8 * (kc & 1);
-        u32x4 pk;
-        pk[0] = pack_bf16x2(s[r0 + 0], s[r0 + 1]);
-        pk[1] = pack_bf16x2(s[r0 + 2], s[r0 + 3]);
-        pk[2] = pack_bf16x2(s[r0 + 4], s[r0 + 5]);
-        pk[3] = pack_bf16x2(s[r0 + 6], s[r0 + 7]);
-        pf[nb] = __builtin_bit_cast(bf16x8, pk);
-      }
-#pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd) {
-        const int d = mbd * 32 + l32, cc = 2 * kc + h;
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + d * BC + (cc ^ swz_v<BC>(d)) * 8);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          oacc[nb][mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb], oacc[nb][mbd], 0, 0, 0);
+      for (int kc = 0; kc < 4; ++kc) {
+        const uint8_t* vb = sb + v_off[mbd] + 16 * kc * C::ROWB;
+        const s16x4 lo = lds_read_tr16(vb);
+        const s16x4 hi = lds_read_tr16(vb + 8 * C::ROWB);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[kc], oacc[mbd], 0, 0, 0);
       }
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    const int kv0 = t * BC;
-    if (kv0 < wave_kv_end) compute_tile(kv0, stage);
-    if (t + 1 < n_tiles) store_tile(stage ^ 1);
+  // One loop iteration per tile: wait for this wave's loads of tile t, barrier (now every wave's loads
+  // of tile t have landed and every wave has finished tile t-1, whose stage is reused), start loading
+  // tile t+1, compute tile t.  The loop is unrolled by two so each stage index is a compile-time value.
+  auto tile = [&](auto stage_tag, int t) {
+    constexpr int STAGE = decltype(stage_tag)::value;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (t + 1 < n_tiles) load_tile(t + 1, STAGE ^ 1);
+    const int kv0 = t * C::BC;
+    if (kv0 < wave_kv_end) {
+      const bool masked = (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off);
+      if (masked)
+        compute_tile(stage_tag, std::true_type{}, kv0);
+      else
+        compute_tile(stage_tag, std::false_type{}, kv0);
+    }
+  };
+
+  load_tile(0, 0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  // epilogue: O / l rounded to bf16 (nearest even), LSE = ln2 * (m + log2 l)
+  // ---------------------------------------------------------------- epilogue
+  // O / l_hat (the weights that entered the value product) rounded to bf16, LSE from the fp32 sum.
+  const float lt = pair_sum(l_run);
+  const float inv = 1.f / pair_sum(lh_run);
+  if (qi < p.Nq) {
+    uint16_t* orow = p.o + head_q + (size_t)qi * D;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float lt = l_run[nb] + xor32(l_run[nb]);
-    const float inv = 1.f / lt;
-    const int qi = qw0 + nb * 32 + l32;
-    if (qi < p.Nq) {
-      uint16_t* orow = p.o + head_q + (size_t)qi * D;
+    for (int mbd = 0; mbd < C::MBD; ++mbd)
 #pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x16& a = oacc[nb][mbd];
-          u32x2 val;
-          val[0] = pack_bf16x2(a[4 * g4 + 0] * inv, a[4 * g4 + 1] * inv);
-          val[1] = pack_bf16x2(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + mbd * 32 + 8 * g4 + 4 * h) = val;
-        }
-      if (h == 0 && p.lse) p.lse[(size_t)bh * p.Nq + qi] = (m_run[nb] + log2_hw(lt)) * kLn2;
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x16& a = oacc[mbd];
+        u32x2 val;
+        val[0] = pack_bf16x2(a[4 * g4 + 0] * inv, a[4 * g4 + 1] * inv);
+        val[1] = pack_bf16x2(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + mbd * 32 + 8 * g4 + 4 * h) = val;
+      }
+    if (h == 0 && p.lse) p.lse[(size_t)bh * p.Nq + qi] = (m_run + log2_hw(lt)) * kLn2;
   }
 }
 
 // ---------------------------------------------------------------------------------------------- launch
 
-namespace {
-constexpr int kNW = 4;
-constexpr int kBC = 64;
-template <int D>
-constexpr int nb_for() { return 1; }
-}  // namespace
-
 int64_t prefill_bf16_grid(int B, int H, int Nq, int d) {
-  const int br = kNW * 32 * (d == 128 ? nb_for<128>() : nb_for<64>());
+  const int br = d == 128 ? Cfg<128>::BR : Cfg<64>::BR;
   return (int64_t)B * H * ((Nq + br - 1) / br);
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
-  constexpr int NB = nb_for<D>();
-  using C = Bf16Cfg<D, NB, kNW, kBC>;
+  using C = Cfg<D>;
   PrefillParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -315,9 +333,9 @@ static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   p.off = a.Nkv - a.Nq;
   p.n_qt = (a.Nq + C::BR - 1) / C::BR;
   p.total = a.B * a.H * p.n_qt;
-  p.c = fabsf(a.scale) * kLog2e;
+  p.c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-126f);
   p.qxor = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NB, kNW, kBC, CAUSAL>), dim3(p.total), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
