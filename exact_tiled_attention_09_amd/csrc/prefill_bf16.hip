@@ -14,7 +14,8 @@
 // sum.  The score tile lives only in registers.
 //
 // gfx950 mapping: one work-group of 4 waves per (batch*head, 128-query tile), 32 query rows per wave,
-// two work-groups per CU (two waves per SIMD: one wave's softmax runs while the other's MFMAs run).
+// two work-groups per CU (two waves per SIMD: one wave's softmax runs while the other's MFMAs run;
+// s_setprio favours the wave that is in an MFMA phase).
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS = A operand, Q^T in VGPRs = B operand): in
 //    the 32x32 result a lane holds one query and 16 keys; lanes l and l^32 together hold the row, so
 //    row max / row sum are in-lane reductions plus one v_permlane32_swap.
@@ -201,7 +202,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     constexpr int STAGE = decltype(stage_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     const uint8_t* sb = smem + STAGE * C::STAGEB;
-    // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks)
+    // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks).  The wave raises its issue
+    // priority for its MFMA phases and drops it for the softmax, so when both waves of a SIMD are
+    // ready the matrix-core work goes first and the other wave's vector work fills in around it.
+    __builtin_amdgcn_s_setprio(1);
     f32x16 S[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -221,6 +225,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
           if (32 * mb + 8 * (r >> 2) + (r & 3) > rel) S[mb][r] = kNegInf;
     }
     // online softmax with the lazy reference maximum
+    __builtin_amdgcn_s_setprio(0);
     float mx = S[0][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[0][r]);
@@ -255,6 +260,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
       for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[mbd] *= alpha;
     }
     // O^T += V^T P^T
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mbd = 0; mbd < C::MBD; ++mbd) {
 #pragma unroll
