@@ -198,9 +198,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
   }
 
   // ---------------------------------------------------------------- one tile
-  auto compute_tile = [&](auto stage_tag, auto masked_tag, int kv0) {
+  auto compute_tile = [&](auto stage_tag, bool masked, int kv0) {
     constexpr int STAGE = decltype(stage_tag)::value;
-    constexpr bool MASKED = decltype(masked_tag)::value;
     const uint8_t* sb = smem + STAGE * C::STAGEB;
     // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks).  The wave raises its issue
     // priority for its MFMA phases and drops it for the softmax, so when both waves of a SIMD are
@@ -215,8 +214,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
         S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
       }
     }
-    // mask (diagonal and ragged-tail tiles only)
-    if constexpr (MASKED) {
+    // mask (diagonal and ragged-tail tiles only; the rest of the tile is one code path)
+    if (masked) {
       const int rel = lim - kv0 - 4 * h;  // key offset within the tile allowed iff 8*(r/4) + (r%4) + 32*mb <= rel
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -283,13 +282,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(t + 1, STAGE ^ 1);
     const int kv0 = t * C::BC;
-    if (kv0 < wave_kv_end) {
-      const bool masked = (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off);
-      if (masked)
-        compute_tile(stage_tag, std::true_type{}, kv0);
-      else
-        compute_tile(stage_tag, std::false_type{}, kv0);
-    }
+    if (kv0 < wave_kv_end)
+      compute_tile(stage_tag, (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off), kv0);
   };
 
   load_tile(0, 0);
