@@ -28,20 +28,23 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-KERNEL_SOURCES = ["exact_tiled_attention_09_amd/csrc/prefill_bf16.hip", "exact_tiled_attention_09_amd/csrc/decode.hip",
-                  "exact_tiled_attention_09_amd/csrc/common.h"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha(path: str) -> str:
-    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
+def source_sha(paths) -> str:
+    """Short hash of the kernel source files (concatenated), to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        h.update(open(os.path.join(ROOT, path), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if the kernel is unchanged since."""
+    """HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by the counters' ratio on a plain
+    copy of known size) from profiles/traffic.json, or None if the kernel source changed since."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -90,6 +93,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "f32"], default="all",
+                    help="launch only this part of the step (for profiler runs); the JSON line is still printed")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the step, run 5 device-to-device copies of this many bytes (calibrates "
+                         "the profiler's HBM byte counters against a copy of known size) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build runs on a single "
@@ -104,6 +112,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "copies": 5}))
+        return
 
     def upload(x, dtype):
         if dtype == "f32":
@@ -111,35 +128,45 @@ def main():
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
 
     wp, wd, w1 = syn.WORKLOADS["c3"], syn.WORKLOADS["c5"], syn.WORKLOADS["c1"]
-    log(f"[bench] generating inputs: {wp.name}, {wd.name}, {w1.name}")
-    pq, pk, pv = (upload(syn.make_tensor(wp, t), "bf16") for t in "qkv")
-    po = torch.empty_like(pq)
-    plse = torch.empty(pq.shape[:-1], dtype=torch.float32, device=dev)
-    dq = upload(syn.make_tensor(wd, "q")[:, :, 0].copy(), "bf16")
-    dk = upload(syn.make_tensor(wd, "k"), "bf16")
-    dv = upload(syn.make_tensor(wd, "v"), "bf16")
-    do = torch.empty_like(dq)
-    dlse = torch.empty(dq.shape[:-1], dtype=torch.float32, device=dev)
+    run_p = args.only in ("all", "prefill")
+    run_d = args.only in ("all", "decode")
+    run_f = args.only in ("all", "f32")
     S = wd.num_splits
-    ws = fa.decode_workspace(wd.B, wd.H, wd.Nkv, wd.d, S, dev)
-    fq, fk, fv = (upload(syn.make_tensor(w1, t), "f32") for t in "qkv")
-    fo = torch.empty_like(fq)
-    flse = torch.empty(fq.shape[:-1], dtype=torch.float32, device=dev)
+    log(f"[bench] generating inputs: {wp.name}, {wd.name}, {w1.name} (only={args.only})")
+    if run_p:
+        pq, pk, pv = (upload(syn.make_tensor(wp, t), "bf16") for t in "qkv")
+        po = torch.empty_like(pq)
+        plse = torch.empty(pq.shape[:-1], dtype=torch.float32, device=dev)
+    if run_d:
+        dq = upload(syn.make_tensor(wd, "q")[:, :, 0].copy(), "bf16")
+        dk = upload(syn.make_tensor(wd, "k"), "bf16")
+        dv = upload(syn.make_tensor(wd, "v"), "bf16")
+        do = torch.empty_like(dq)
+        dlse = torch.empty(dq.shape[:-1], dtype=torch.float32, device=dev)
+        ws = fa.decode_workspace(wd.B, wd.H, wd.Nkv, wd.d, S, dev)
+    if run_f:
+        fq, fk, fv = (upload(syn.make_tensor(w1, t), "f32") for t in "qkv")
+        fo = torch.empty_like(fq)
+        flse = torch.empty(fq.shape[:-1], dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.fa_fwd(pq, pk, pv, po, plse, wp.scale, True, stream)
+        if run_p:
+            fa.fa_fwd(pq, pk, pv, po, plse, wp.scale, True, stream)
         if ev is not None:
             ev[1].record(stream)
-        fa.fa_decode_split(dq, dk, dv, wd.scale, S, ws, stream)
+        if run_d:
+            fa.fa_decode_split(dq, dk, dv, wd.scale, S, ws, stream)
         if ev is not None:
             ev[2].record(stream)
-        fa.fa_decode_combine(ws, do, dlse, S, stream)
+        if run_d:
+            fa.fa_decode_combine(ws, do, dlse, S, stream)
         if ev is not None:
             ev[3].record(stream)
-        fa.fa_fwd(fq, fk, fv, fo, flse, w1.scale, False, stream)
+        if run_f:
+            fa.fa_fwd(fq, fk, fv, fo, flse, w1.scale, False, stream)
         if ev is not None:
             ev[4].record(stream)
 
@@ -160,11 +187,12 @@ def main():
     t_prefill, t_split, t_comb, t_f32 = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
     t_step = ms(0, 4)
 
-    pf_tflops = wp.flops / (t_prefill.mean() * 1e-3) / 1e12
+    rate = lambda work, ms_: work / (ms_ * 1e-3) if ms_ > 0 else 0.0  # noqa: E731
+    pf_tflops = rate(wp.flops, t_prefill.mean()) / 1e12
     split_bytes = 2 * wd.B * wd.H * wd.Nkv * wd.d * 2 + wd.B * wd.H * wd.d * 2   # K, V, q read once
-    split_gbs = split_bytes / (t_split.mean() * 1e-3) / 1e9
-    dec_gbs = wd.io_bytes / ((t_split.mean() + t_comb.mean()) * 1e-3) / 1e9
-    f32_tflops = w1.flops / (t_f32.mean() * 1e-3) / 1e12
+    split_gbs = rate(split_bytes, t_split.mean()) / 1e9
+    dec_gbs = rate(wd.io_bytes, t_split.mean() + t_comb.mean()) / 1e9
+    f32_tflops = rate(w1.flops, t_f32.mean()) / 1e12
 
     rec = {
         "metric": "prefill TFLOP/s & % bf16 MFMA peak; decode KV-read GB/s & % HBM peak",
@@ -219,8 +247,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "gpu": torch.cuda.get_device_name(0),
     }
-    del pq, pk, pv, dk, dv
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.only == "all":
         log("[bench] timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline()
     else:
