@@ -7,9 +7,10 @@
 //   x_ij = s_ij * c  (c = |scale| * log2 e: exp2 with log2 e folded into the scale is the same exp)
 //   m' = max(m, max_j x_ij),  p_ij = 2^(x_ij - m'),  l = 2^(m - m') l + sum_j p_ij,
 //   O = 2^(m - m') O + sum_j p_ij v_j;   at the end O / l and LSE = ln2 * (m + log2 l).
-// The running maximum is moved only when a tile's maximum exceeds it by more than kTau (log2 units),
-// so every exponent stays <= kTau and O, l need rescaling only on those rare moves; O / l and LSE do
-// not depend on which reference maximum is used.  O is normalised by the sum of the same bf16
+// The reference maximum m is set from the first tile and afterwards moved only when a tile's weights
+// 2^(x - m) would exceed 2^64; other tiles skip the max reduction entirely and O, l are rescaled only
+// on those rare moves.  O / l and the LSE do not depend on which reference is used (exact arithmetic),
+// and 2^64 keeps every sum far from fp32 overflow.  O is normalised by the sum of the same bf16
 // weights that entered the value product (so a dominant weight cancels exactly), the LSE by the fp32
 // sum.  The score tile lives only in registers.
 //
@@ -50,14 +51,24 @@ struct PrefillParams {
   uint32_t qxor;  // 0x80008000 when scale < 0: q is negated on load (exact) so that c > 0
 };
 
-constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units (p <= 2^8)
+#ifndef FA_NW
+#define FA_NW 4
+#endif
+#ifndef FA_BC
+#define FA_BC 64
+#endif
+#ifndef FA_OCC
+#define FA_OCC 2
+#endif
+constexpr float kBig = 0x1p64f;  // weights above this trigger a move of the reference maximum
 
 template <int D>
 struct Cfg {
-  static constexpr int NW = 4;             // waves per work-group
+  static constexpr int NW = FA_NW;         // waves per work-group
   static constexpr int NT = NW * 64;       // threads
   static constexpr int BR = NW * 32;       // query rows per work-group (32 per wave)
-  static constexpr int BC = 64;            // keys per tile
+  static constexpr int BC = FA_BC;         // keys per tile
+  static constexpr int NBLK = BC / 32;     // 32-key score blocks per tile
   static constexpr int ROWB = 2 * D;       // bytes per K / V row
   static constexpr int CH = D / 8;         // 16-byte chunks per row
   static constexpr int TILEB = BC * ROWB;  // bytes per K (or V) tile
@@ -68,7 +79,7 @@ struct Cfg {
   static constexpr int KS = D / 16;        // MFMA k-steps over d
   static constexpr int MBD = D / 32;       // 32-wide d blocks of O^T
   static_assert(TILEB % (NT * 16) == 0, "tile loads must divide evenly");
-  static_assert(NSTAGE * STAGEB <= 65536, "fragment reads use 16-bit immediate offsets");
+  // fragment reads use 16-bit immediate offsets when NSTAGE * STAGEB <= 64 KB
 };
 
 // 16-byte-chunk XOR swizzles within a row, chosen so that the fragment reads below hit distinct banks:
@@ -114,7 +125,7 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
+__global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(PrefillParams p) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NSTAGE * C::STAGEB];
 
@@ -205,11 +216,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     // priority for its MFMA phases and drops it for the softmax, so when both waves of a SIMD are
     // ready the matrix-core work goes first and the other wave's vector work fills in around it.
     __builtin_amdgcn_s_setprio(1);
-    f32x16 S[2] = {f32x16{}, f32x16{}};
+    f32x16 S[C::NBLK];
+#pragma unroll
+    for (int mb = 0; mb < C::NBLK; ++mb) S[mb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < C::NBLK; ++mb) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + k_off[ks] + mb * 32 * C::ROWB);
         S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
       }
@@ -218,52 +231,66 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     if (masked) {
       const int rel = lim - kv0 - 4 * h;  // key offset within the tile allowed iff 8*(r/4) + (r%4) + 32*mb <= rel
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::NBLK; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (32 * mb + 8 * (r >> 2) + (r & 3) > rel) S[mb][r] = kNegInf;
     }
-    // online softmax with the lazy reference maximum
+    // Online softmax against the running reference maximum m: the weights are 2^(x - m).  Only the
+    // first tile of a wave (m = -inf) and tiles whose weights would exceed 2^64 reduce the tile's
+    // maximum, move m and rescale O, l; every other tile skips the max reduction (O / l and the LSE do
+    // not depend on which reference is used, and 2^64 keeps every sum far from fp32 overflow).
     __builtin_amdgcn_s_setprio(0);
-    float mx = S[0][0];
+    float rs, rsh;
+    bf16x8 P[2 * C::NBLK];
+    auto weights = [&](float mref) {
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      rsh = 0.f;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[0][r]);
+      for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
+        float pr[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[1][r]);
-    mx = pair_max(mx);
-    const float mt = mx * c;
-    const bool up = mt > m_run + kTau;
-    const float mn = up ? mt : m_run;
-    const float alpha = up ? exp2_hw(m_run - mn) : 1.f;
-    m_run = mn;
-    float rs = 0.f, rsh = 0.f;
-    bf16x8 P[4];
+        for (int i = 0; i < 8; ++i) {
+          pr[i] = exp2_hw(fmaf(S[kc >> 1][8 * (kc & 1) + i], c, -mref));
+          part[i & 3] += pr[i];
+        }
+        u32x4 pk;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      float pr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = exp2_hw(fmaf(S[kc >> 1][8 * (kc & 1) + i], c, -mn));
-        rs += pr[i];
+        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+        P[kc] = __builtin_bit_cast(bf16x8, pk);
+        rsh = sum_bf16x8(P[kc], rsh);
       }
-      u32x4 pk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
-      P[kc] = __builtin_bit_cast(bf16x8, pk);
-      rsh = sum_bf16x8(P[kc], rsh);
+      rs = (part[0] + part[1]) + (part[2] + part[3]);
+    };
+    bool slow = __builtin_amdgcn_ballot_w64(m_run == kNegInf) != 0;
+    if (!slow) {
+      weights(m_run);
+      slow = __builtin_amdgcn_ballot_w64(!(rs <= kBig)) != 0;  // also true for inf / nan
     }
-    l_run = alpha * l_run + rs;
-    lh_run = alpha * lh_run + rsh;
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    float alpha = 1.f;
+    if (slow) {
+      float mx = S[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[0][r]);
+#pragma unroll
+      for (int mb = 1; mb < C::NBLK; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mb][r]);
+      const float mn = fmaxf(m_run, pair_max(mx) * c);
+      alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - mn);
+      m_run = mn;
+      weights(mn);
 #pragma unroll
       for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[mbd] *= alpha;
     }
+    l_run = alpha * l_run + rs;
+    lh_run = alpha * lh_run + rsh;
     // O^T += V^T P^T
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mbd = 0; mbd < C::MBD; ++mbd) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+      for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
         const uint8_t* vb = sb + v_off[mbd] + 16 * kc * C::ROWB;
         const s16x4 lo = lds_read_tr16(vb);
         const s16x4 hi = lds_read_tr16(vb + 8 * C::ROWB);
