@@ -74,6 +74,10 @@ fa_status check_fwd(const void* q, const void* k, const void* v, void* o, float*
   int64_t nq_el, nkv_el;
   if (!mul_ok(nq_el, {B, H, N_q, d}) || !mul_ok(nkv_el, {B, H, N_kv, d}) || nq_el > kMaxElems || nkv_el > kMaxElems)
     return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
+  // the bf16 kernel addresses one head's K and V through 32-bit buffer byte ranges
+  if (dtype == FA_DTYPE_BF16 && (int64_t)N_kv * d * 2 > INT_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "bf16 prefill supports N_kv * d * 2 <= 2^31 - 1 bytes per head (got N_kv=%d, d=%d)",
+                N_kv, d);
   const int64_t grid = dtype == FA_DTYPE_BF16 ? fa::prefill_bf16_grid(B, H, N_q, d) : fa::prefill_f32_grid(B, H, N_q, d);
   if (grid > INT_MAX) return fail(FA_ERR_INVALID_ARG, "launch grid too large (%lld work-groups)", (long long)grid);
   const Range rq = span(q, nq_el * *esz), rk = span(k, nkv_el * *esz), rv = span(v, nkv_el * *esz);

@@ -91,9 +91,14 @@ template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // One wave-wide direct global -> LDS load of 16 bytes per lane into lds_block + 16 * lane.
-__device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
+// Buffer resource over `bytes` bytes at `base` (raw buffer: stride 0, byte offsets).  Loads at offsets
+// at or past `bytes` return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes per lane from rsrc + voff into LDS: the wave's 64 x 16 bytes land contiguously at lds_block.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, int voff, void* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, 0, 0, 0);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
   int qt = lid - bh * p.n_qt;
   if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
   const int q0 = qt * C::BR;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const size_t head_q = (size_t)bh * p.Nq * D;
   const size_t head_kv = (size_t)bh * p.Nkv * D;
@@ -169,25 +174,27 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
 
   // ---------------------------------------------------------------- global -> LDS (direct, no registers)
   // Load i of wave w fills the 1 KB block (w * LPT + i) of a tile: rows RPL*(w*LPT+i) + lane/CH, physical
-  // chunk lane%CH, which holds logical chunk (lane%CH) ^ swizzle(row).  Rows past N_kv re-read the last
-  // row (finite values; their scores are masked, so they carry zero weight).
-  int ld_row[C::LPT], ld_ck[C::LPT], ld_cv[C::LPT];
+  // chunk lane%CH, which holds logical chunk (lane%CH) ^ swizzle(row).  The per-lane byte offsets within
+  // a tile are fixed; each tile gets a buffer resource starting at its first key and ending at N_kv, so
+  // the loads need no vector address arithmetic and rows past N_kv read zeros (their scores are masked).
+  int ld_k[C::LPT], ld_v[C::LPT];
 #pragma unroll
   for (int i = 0; i < C::LPT; ++i) {
     const int r = C::RPL * (w * C::LPT + i) + lane / C::CH, pc = lane % C::CH;
-    ld_row[i] = r;
-    ld_ck[i] = (pc ^ swz_k<D>(r)) * 8;
-    ld_cv[i] = (pc ^ swz_v<D>(r)) * 8;
+    ld_k[i] = r * C::ROWB + 16 * (pc ^ swz_k<D>(r));
+    ld_v[i] = r * C::ROWB + 16 * (pc ^ swz_v<D>(r));
   }
   auto load_tile = [&](int t, int stage) {
     const int kv0 = t * C::BC;
+    const int bytes = (p.Nkv - kv0) * C::ROWB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
     uint8_t* st = smem + stage * C::STAGEB;
 #pragma unroll
     for (int i = 0; i < C::LPT; ++i) {
-      const size_t row = (size_t)min(kv0 + ld_row[i], p.Nkv - 1) * D;
       uint8_t* blk = st + 1024 * (w * C::LPT + i);
-      load_lds16(kg + row + ld_ck[i], blk);
-      load_lds16(vg + row + ld_cv[i], blk + C::TILEB);
+      load_lds16(rk, ld_k[i], blk);
+      load_lds16(rv, ld_v[i], blk + C::TILEB);
     }
   };
 

@@ -64,6 +64,8 @@ typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 } fa_dtype;
  * bf16: scores and value sums accumulate in fp32 on the matrix cores, the
  * softmax runs in fp32, the probabilities enter the value product as bf16 and
  * o is rounded to bf16 to nearest-even.  f32: fp32 throughout.
+ * bf16 additionally needs N_kv * d * 2 <= 2^31 - 1 (one head's K or V within a
+ * 32-bit byte range); larger heads return FA_ERR_UNSUPPORTED.
  * Passage: the attention equation and "How FlashAttention Works" of the page
  * named at the top; prefill is "Where you actually feel it" of "Flash Attention
  * Explained: Same Maths, Far Less Memory".

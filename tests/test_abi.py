@@ -72,6 +72,7 @@ def fwd(L, q=P(0), k=P(1), v=P(2), o=P(3), lse=P(4), B=1, H=1, Nq=8, Nkv=8, d=64
     (dict(d=0), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nkv=1 << 23, d=128), fa.FA_ERR_UNSUPPORTED),            # one head's K past a 32-bit byte range
     (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(causal=1, Nq=9, Nkv=8), fa.FA_ERR_INVALID_ARG),
