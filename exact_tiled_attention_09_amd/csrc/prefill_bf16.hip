@@ -24,9 +24,10 @@
 //    rounded to bf16, keys contracted in the order the score layout gives them; V^T (A operand) is
 //    read from row-major V in LDS with ds_read_b64_tr_b16, whose 16-lane transpose delivers 4 keys at
 //    one d per lane, in exactly that key order.
-//  * K and V tiles of 64 keys go global -> LDS with direct 16-byte loads (global_load_lds_dwordx4, no
-//    staging registers), double-buffered with one barrier per tile: tile t+1 is in flight while tile t
-//    is computed.  16-byte chunks are XOR-swizzled within each row (the swizzle is applied through
+//  * K and V tiles of 64 keys go global -> LDS with direct 16-byte loads (buffer_load_dwordx4 ... lds,
+//    no staging registers), double-buffered with one barrier per tile: tile t+1 is in flight while
+//    tile t is computed.  The loads of tile t+1 are issued right after the S MFMAs of tile t, so they
+//    land during the softmax rather than during fragment reads.  16-byte chunks are XOR-swizzled within each row (the swizzle is applied through
 //    each lane's source address) so every fragment read hits distinct banks, and fragment addresses
 //    are per-lane bases plus compile-time offsets.
 //  * Causal tiles above the diagonal are never loaded; a wave skips the math of tiles that lie fully
@@ -90,7 +91,6 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// One wave-wide direct global -> LDS load of 16 bytes per lane into lds_block + 16 * lane.
 // Buffer resource over `bytes` bytes at `base` (raw buffer: stride 0, byte offsets).  Loads at offsets
 // at or past `bytes` return zeros instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
@@ -216,7 +216,10 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
   }
 
   // ---------------------------------------------------------------- one tile
-  auto compute_tile = [&](auto stage_tag, bool masked, int kv0) {
+  // `next()` issues this wave's loads of the next tile.  It runs right after the S MFMAs are issued, so
+  // the data lands in LDS during the softmax, when the wave reads no fragments (direct LDS writes that
+  // land during the fragment reads of the MFMA phases slow those reads down).
+  auto compute_tile = [&](auto stage_tag, bool masked, int kv0, auto&& next) {
     constexpr int STAGE = decltype(stage_tag)::value;
     const uint8_t* sb = smem + STAGE * C::STAGEB;
     // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks).  The wave raises its issue
@@ -234,6 +237,7 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
         S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
       }
     }
+    next();
     // mask (diagonal and ragged-tail tiles only; the rest of the tile is one code path)
     if (masked) {
       const int rel = lim - kv0 - 4 * h;  // key offset within the tile allowed iff 8*(r/4) + (r%4) + 32*mb <= rel
@@ -314,10 +318,15 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
     constexpr int STAGE = decltype(stage_tag)::value;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1, STAGE ^ 1);
+    const bool more = t + 1 < n_tiles;
+    auto next = [&]() {
+      if (more) load_tile(t + 1, STAGE ^ 1);
+    };
     const int kv0 = t * C::BC;
     if (kv0 < wave_kv_end)
-      compute_tile(stage_tag, (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off), kv0);
+      compute_tile(stage_tag, (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off), kv0, next);
+    else if (more)
+      load_tile(t + 1, STAGE ^ 1);
   };
 
   load_tile(0, 0);
