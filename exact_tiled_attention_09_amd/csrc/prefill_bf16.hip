@@ -132,7 +132,11 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(PrefillParams p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NSTAGE * C::STAGEB];
+  // One LDS array per stage and operand: the compiler can then tell that the direct loads into one
+  // stage do not alias the fragment reads of the other, and does not wait for those loads before them.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[C::TILEB], lds_v0[C::TILEB], lds_k1[C::TILEB], lds_v1[C::TILEB];
+  auto kbuf = [&](int st) -> uint8_t* { return st == 0 ? lds_k0 : lds_k1; };
+  auto vbuf = [&](int st) -> uint8_t* { return st == 0 ? lds_v0 : lds_v1; };
 
   const int lid = xcd_logical_id(blockIdx.x, p.total);
   const int bh = lid / p.n_qt;
@@ -189,12 +193,11 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
     const int bytes = (p.Nkv - kv0) * C::ROWB;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
-    uint8_t* st = smem + stage * C::STAGEB;
 #pragma unroll
     for (int i = 0; i < C::LPT; ++i) {
-      uint8_t* blk = st + 1024 * (w * C::LPT + i);
-      load_lds16(rk, ld_k[i], blk);
-      load_lds16(rv, ld_v[i], blk + C::TILEB);
+      const int blk = 1024 * (w * C::LPT + i);
+      load_lds16(rk, ld_k[i], kbuf(stage) + blk);
+      load_lds16(rv, ld_v[i], vbuf(stage) + blk);
     }
   };
 
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
 #pragma unroll
   for (int mbd = 0; mbd < C::MBD; ++mbd) {
     const int d0 = 32 * mbd + 16 * tr_dh + 4 * (tr_j & 3);
-    v_off[mbd] = C::TILEB + tr_row * C::ROWB + 16 * ((d0 >> 3) ^ swz_v<D>(tr_row)) + 2 * (d0 & 7);
+    v_off[mbd] = tr_row * C::ROWB + 16 * ((d0 >> 3) ^ swz_v<D>(tr_row)) + 2 * (d0 & 7);
   }
 
   // ---------------------------------------------------------------- one tile
@@ -221,7 +224,8 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
   // land during the fragment reads of the MFMA phases slow those reads down).
   auto compute_tile = [&](auto stage_tag, bool masked, int kv0, auto&& next) {
     constexpr int STAGE = decltype(stage_tag)::value;
-    const uint8_t* sb = smem + STAGE * C::STAGEB;
+    const uint8_t* sb = kbuf(STAGE);
+    const uint8_t* svb = vbuf(STAGE);
     // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks).  The wave raises its issue
     // priority for its MFMA phases and drops it for the softmax, so when both waves of a SIMD are
     // ready the matrix-core work goes first and the other wave's vector work fills in around it.
@@ -296,13 +300,14 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
     }
     l_run = alpha * l_run + rs;
     lh_run = alpha * lh_run + rsh;
-    // O^T += V^T P^T
+    // O^T += V^T P^T, one 16-key chunk at a time across the d blocks (independent accumulators back to
+    // back, so no MFMA waits for the previous one's result)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int mbd = 0; mbd < C::MBD; ++mbd) {
+    for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
 #pragma unroll
-      for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
-        const uint8_t* vb = sb + v_off[mbd] + 16 * kc * C::ROWB;
+      for (int mbd = 0; mbd < C::MBD; ++mbd) {
+        const uint8_t* vb = svb + v_off[mbd] + 16 * kc * C::ROWB;
         const s16x4 lo = lds_read_tr16(vb);
         const s16x4 hi = lds_read_tr16(vb + 8 * C::ROWB);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
