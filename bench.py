@@ -57,6 +57,57 @@ def traffic_from_profiles(kernel: str):
         return None
 
 
+TRAFFIC_KERNELS = {
+    # name in traffic.json: (run directory prefix, kernel-name substring, kernel sources)
+    "prefill_bf16_c3": ("prefill", "prefill_bf16_kernel",
+                        ["exact_tiled_attention_09_amd/csrc/prefill_bf16.hip", "exact_tiled_attention_09_amd/csrc/common.h"]),
+    "decode_split_c5": ("decode", "decode_split_kernel",
+                        ["exact_tiled_attention_09_amd/csrc/decode.hip", "exact_tiled_attention_09_amd/csrc/common.h"]),
+}
+
+
+def write_traffic(run_dir: str, copy_bytes: int = 1 << 30):
+    """Build profiles/traffic.json from rocprofv3 --pmc runs of this script: <run_dir>/<prefix>.<COUNTER>/
+    holding p_counter_collection.csv for prefix copy (--copy-bytes), prefill (--only prefill) and decode
+    (--only decode), COUNTER in FETCH_SIZE, WRITE_SIZE.  The copy of known size gives the factor that turns
+    each counter's KiB into bytes."""
+    import csv
+    import glob
+    import synthetic as syn
+
+    def per_dispatch(prefix, counter, kernel):
+        vals = {}
+        for f in glob.glob(os.path.join(run_dir, f"{prefix}.{counter}", "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no {counter} samples for {kernel} under {run_dir}/{prefix}.{counter}")
+        return sum(vals.values()) / len(vals), len(vals)
+
+    # the runtime's device-to-device copy kernel (not the fill that initialises the source): per dispatch it
+    # reads and writes copy_bytes
+    fetch_copy, _ = per_dispatch("copy", "FETCH_SIZE", "copyBuffer")
+    write_copy, _ = per_dispatch("copy", "WRITE_SIZE", "copyBuffer")
+    rf, wf = copy_bytes / (fetch_copy * 1024), copy_bytes / (write_copy * 1024)
+    out = {"_calibration": {"copy_bytes": copy_bytes, "fetch_kib": fetch_copy, "write_kib": write_copy,
+                            "read_factor": rf, "write_factor": wf,
+                            "note": "device-to-device copy of copy_bytes: bytes = counter KiB * 1024 * factor"}}
+    wp, wd = syn.WORKLOADS["c3"], syn.WORKLOADS["c5"]
+    alg = {"prefill_bf16_c3": wp.io_bytes,
+           "decode_split_c5": 2 * wd.B * wd.H * wd.Nkv * wd.d * 2 + wd.B * wd.H * wd.d * 2}
+    for name, (prefix, kernel, sources) in TRAFFIC_KERNELS.items():
+        fk, n = per_dispatch(prefix, "FETCH_SIZE", kernel)
+        wk, _ = per_dispatch(prefix, "WRITE_SIZE", kernel)
+        rb, wb = fk * 1024 * rf, wk * 1024 * wf
+        out[name] = {"source": sources, "source_sha": source_sha(sources), "fetch_kib": fk, "write_kib": wk,
+                     "read_bytes": rb, "write_bytes": wb, "bytes_per_launch": rb + wb,
+                     "algorithmic_bytes": alg[name], "dispatches": n}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(target_s: float = 12.0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the causal prefill workload."""
     import synthetic as syn
@@ -98,7 +149,13 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the step, run 5 device-to-device copies of this many bytes (calibrates "
                          "the profiler's HBM byte counters against a copy of known size) and exit")
+    ap.add_argument("--write-traffic", metavar="RUN_DIR",
+                    help="no GPU work: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script under RUN_DIR into "
+                         "profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build runs on a single "
               f"MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
