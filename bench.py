@@ -108,6 +108,39 @@ def write_traffic(run_dir: str, copy_bytes: int = 1 << 30):
     print(json.dumps(out, indent=1))
 
 
+def time_events(fn, stream, steps: int, warmup: int):
+    """Average duration (ms) of fn() over `steps` calls, each bracketed by HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+
+def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int):
+    """Workloads beyond the graded step (timed after it, not part of ms_per_step)."""
+    import torch
+    out = {}
+    w = syn.NEXT_WORKLOADS["chunk"]
+    log(f"[bench] next: {w.name}")
+    q, k, v = (upload(syn.make_tensor(w, t), "bf16") for t in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    t = time_events(lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream), stream, steps, warmup)
+    out["chunked_prefill"] = {"workload": "fa_fwd causal (bottom-right) bf16 B1 H32 N_q1000 N_kv8192 d128",
+                              "value": round(w.flops / (t * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                              "frac_of_peak": round(w.flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "avg_kernel_ms": round(t, 4)}
+    del q, k, v, o, lse
+    return out
+
+
 def cpu_baseline(target_s: float = 12.0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the causal prefill workload."""
     import synthetic as syn
@@ -144,7 +177,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "f32"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "f32", "next"], default="all",
                     help="launch only this part of the step (for profiler runs); the JSON line is still printed")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the step, run 5 device-to-device copies of this many bytes (calibrates "
@@ -304,6 +337,8 @@ def main():
         "wall_s_timed": round(wall, 4),
         "gpu": torch.cuda.get_device_name(0),
     }
+    if args.only in ("all", "next"):
+        rec["next"] = time_next(fa, syn, upload, dev, stream, args.steps, args.warmup)
     if not args.no_cpu_baseline and args.only == "all":
         log("[bench] timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline()

@@ -1,6 +1,7 @@
 """CPU fp64 oracle (test infrastructure only; never imported by the product path)."""
 from .attention import (  # noqa: F401
     allowed_mask,
+    attention_bwd_ref,
     attention_ref,
     combine_ref,
     decode_ref,

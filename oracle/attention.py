@@ -25,6 +25,16 @@ What it computes (the plain definition, written out):
 Large inputs are processed in panels of complete rows: every row is still the
 full-row softmax; no online merge is involved.
 
+The backward pass (``attention_bwd_ref``) is the plain derivative of that same
+function for an upstream gradient dO, written out on materialised matrices
+(training needs these gradients -- "FlashAttention Explained: How AI Models
+Process Attention Faster and Use Less Memory", section "FlashAttention in AI
+Training", "More Efficient Backpropagation"; the method recomputes the
+probabilities instead of storing them, "How FlashAttention Speeds Up LLM
+Attention", table of contents).  With P the row softmax of S = scale*Q K^T:
+dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)), dQ = scale*dS K,
+dK = scale*dS^T Q.
+
 Two further functions model the method itself and are used only to pin the
 merge rules against the plain definition (they are never what the GPU result is
 compared with):
@@ -55,6 +65,7 @@ __all__ = [
     "split_partials_ref",
     "combine_ref",
     "decode_ref",
+    "attention_bwd_ref",
 ]
 
 
@@ -235,6 +246,30 @@ def decode_ref(q, k, v, scale: float):
         q = q[:, :, None, :]
     o, lse = attention_ref(q, k, v, scale, False)
     return o[:, :, 0], lse[:, :, 0]
+
+
+def attention_bwd_ref(q, k, v, do, scale: float, causal: bool):
+    """Gradients (dQ, dK, dV) of O = softmax(scale Q K^T) V for the upstream gradient dO, fp64.
+
+    q, do: [B,H,N_q,d]; k, v: [B,H,N_kv,d].  Each (b, h) materialises S, P, dP and dS in full
+    (small and medium inputs only).  Masked positions have P = 0, so they carry no gradient.
+    """
+    q, k, v, do = _as4(q), _as4(k), _as4(v), _as4(do)
+    B, H, n_q, d = q.shape
+    n_kv = k.shape[2]
+    if k.shape[:2] != (B, H) or v.shape[:3] != (B, H, n_kv) or do.shape != (B, H, n_q, v.shape[3]):
+        raise ValueError("shape mismatch between q, k, v, do")
+    mask = allowed_mask(n_q, n_kv, causal)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            P, _ = _softmax_panel(scale * (q[b, h] @ k[b, h].T), mask)
+            dv[b, h] = P.T @ do[b, h]
+            dP = do[b, h] @ v[b, h].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dq[b, h] = scale * (dS @ k[b, h])
+            dk[b, h] = scale * (dS.T @ q[b, h])
+    return dq, dk, dv
 
 
 def default_scale(d: int) -> float:

@@ -83,6 +83,18 @@ def test_workload_sampled_rows(cfg):
     assert np.abs(O).max() <= vmax + TOL_O[w.dtype]
 
 
+def test_chunked_prefill_workload():
+    """1000 new queries against an 8192-key cache (bottom-right causal): every row of three heads."""
+    w = syn.NEXT_WORKLOADS["chunk"]
+    host, f64 = inputs(w)
+    O, L = run_fwd(w, host)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    for h in sorted({0, w.H // 2, w.H - 1}):
+        sl = slice(h, h + 1)
+        Oref, Lref = attention_ref(f64["q"][:, sl], f64["k"][:, sl], f64["v"][:, sl], w.scale, w.causal)
+        check(w, O[:, sl], L[:, sl], Oref, Lref, f" head {h}")
+
+
 def test_decode_workload_sampled():
     w = syn.WORKLOADS["c5"]
     print(f"[fa_decode] generating {w.name}", flush=True)
