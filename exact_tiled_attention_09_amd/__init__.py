@@ -51,13 +51,16 @@ def lib() -> ctypes.CDLL:
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp, i]
     L.fa_decode_split.argtypes = [vp, vp, vp, i, i, i, i, f, i, vp, sz, vp, i]
     L.fa_decode_combine.argtypes = [vp, sz, vp, vp, i, i, i, i, vp, i]
+    L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+    L.fa_bwd_workspace_bytes.restype = sz
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp, i]
     L.fa_status_str.argtypes = [i]
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_last_error.argtypes = []
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = ctypes.c_char_p
     for name in ("fa_fwd", "fa_fwd_bf16", "fa_fwd_f32", "fa_decode", "fa_decode_split", "fa_decode_combine",
-                 "fa_decode_num_splits"):
+                 "fa_decode_num_splits", "fa_bwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -171,6 +174,26 @@ def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None):
     _check(st, "fa_decode_combine")
 
 
+def fa_bwd_workspace_bytes(B: int, H: int, N_q: int) -> int:
+    return lib().fa_bwd_workspace_bytes(B, H, N_q)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
+    """libfa fa_bwd: q, o, dout, dq [B,H,N_q,d]; k, v, dk, dv [B,H,N_kv,d] (bf16); lse [B,H,N_q] fp32 as
+    fa_fwd wrote it; workspace a byte device tensor of at least fa_bwd_workspace_bytes()."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    for name, t, n in (("o", o, Nq), ("dout", dout, Nq), ("dq", dq, Nq), ("k", k, Nkv), ("v", v, Nkv),
+                       ("dk", dk, Nkv), ("dv", dv, Nkv)):
+        _check_tensor(name, t, (B, H, n, d), q.dtype)
+    _check_tensor("lse", lse, (B, H, Nq), torch.float32)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, H, Nq, Nkv, d, float(scale), int(bool(causal)), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _stream(stream), _dtype_code(q))
+    _check(st, "fa_bwd")
+
+
 # ----------------------------------------------------------------------------- allocation helpers
 
 def attention(q, k, v, scale: float | None = None, causal: bool = False, stream=None):
@@ -203,3 +226,15 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, workspace=N
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     fa_decode(q, k, v, o, lse, scale, num_splits, workspace, stream)
     return o, lse
+
+
+def attention_backward(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False, stream=None):
+    """Allocate dq, dk, dv and the workspace and run fa_bwd; returns (dq, dk, dv)."""
+    import torch
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B, H, Nq, _ = q.shape
+    ws = torch.empty(fa_bwd_workspace_bytes(B, H, Nq), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, causal, ws, stream)
+    return dq, dk, dv

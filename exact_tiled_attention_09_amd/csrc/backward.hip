@@ -1,0 +1,462 @@
+// Attention backward for gfx950: gradients dQ, dK, dV of O = softmax(scale Q K^T) V, bf16 in / bf16 out,
+// fp32 accumulation.
+//
+// The probabilities are recomputed from Q, K and the forward's log-sum-exp instead of being stored
+// ("How FlashAttention Speeds Up LLM Attention", table of contents: recompute probabilities for
+// training; "FlashAttention Explained: How AI Models Process Attention Faster and Use Less Memory",
+// "FlashAttention in AI Training", "More Efficient Backpropagation").  With the LSE known, a tile's
+// probabilities are final at once: P = 2^(s*c - LSE*log2 e), c = scale*log2 e.  The gradients are the
+// plain derivative of the attention function:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = rowsum(dO_i * O_i) = rowsum(P_i * dP_i),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// Two kernels, no atomics (every output element is summed by one lane, in a fixed order):
+//  * bwd_dq_kernel: one work-group per (b, h, 128 queries); the layout of the forward kernel (S^T = K Q^T
+//    with a lane pair per query).  It also computes D from dO and O and stores it for the next kernel.
+//    Per 64-key tile: S^T = K Q^T and dP^T = V dO^T (K, V fragments from LDS), dS^T in registers,
+//    dQ^T += K^T dS^T (K^T through ds_read_b64_tr_b16 of the same K tile).
+//  * bwd_dkdv_kernel: one work-group per (b, h, 128 keys), the same layout with the roles of queries and
+//    keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query tile streamed through LDS:
+//    S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through transposing reads).
+// Tiles read both row-wise (ds_read_b128) and transposed (ds_read_b64_tr_b16) use a swizzle that keeps
+// both access patterns on distinct banks.
+#include "common.h"
+#include "kernels.h"
+#include "lds_tiles.h"
+
+namespace fa {
+
+struct BwdParams {
+  const uint16_t* __restrict__ q;
+  const uint16_t* __restrict__ k;
+  const uint16_t* __restrict__ v;
+  const uint16_t* __restrict__ o;
+  const uint16_t* __restrict__ dout;
+  const float* __restrict__ lse;
+  float* __restrict__ delta;  // D [B,H,N_q], written by bwd_dq_kernel, read by bwd_dkdv_kernel
+  uint16_t* __restrict__ dq;
+  uint16_t* __restrict__ dk;
+  uint16_t* __restrict__ dv;
+  int Nq, Nkv, off;
+  int n_qt, n_kt;            // 128-query / 128-key blocks per (b, h)
+  int total_q, total_k;      // work-groups of the two kernels
+  float c;                   // scale * log2(e) (any sign)
+  float scale;
+};
+
+template <int D>
+struct BwdCfg {
+  static constexpr int NW = 4, NT = 256;
+  static constexpr int BR = 128;           // queries (dQ kernel) or keys (dK/dV kernel) per work-group
+  static constexpr int BC = 64;            // keys per tile in the dQ kernel
+  static constexpr int BQ = 32;            // queries per tile in the dK/dV kernel
+  static constexpr int ROWB = 2 * D, CH = D / 8, KS = D / 16, MBD = D / 32, RPL = 1024 / ROWB;
+  static constexpr int NBLK = BC / 32;
+  static constexpr int TKV = BC * ROWB, TQ = BQ * ROWB;
+  static constexpr int LPT_KV = TKV / (NT * 16), LPT_Q = TQ / (NT * 16);
+  static_assert(TKV % (NT * 16) == 0 && TQ % (NT * 16) == 0, "tile loads must divide evenly");
+};
+
+// Row swizzle (16-byte chunk XOR) for tiles that are read both as MFMA rows (32 lanes, 32 rows, one
+// logical chunk) and through ds_read_b64_tr_b16 (16 lanes, 4 consecutive rows, two adjacent chunks):
+// rows that meet in one read get chunks in distinct bank groups in both patterns.
+template <int D>
+__device__ __forceinline__ int swz_kv(int r) {
+  return D == 128 ? (((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1))
+                  : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Per-lane LDS byte offsets of the two transposing reads (u = 0, 1: rows 8u + 4h + j/4 of a 16-row
+// chunk) for the d block mbd: lane i of each 16-lane group then holds element [row0 + t][32 mbd + 16 dh
+// + i], t = 0..3, the A-operand layout of a 32-row (d) by 16-column (rows of the tile) MFMA fragment.
+template <int D>
+__device__ __forceinline__ int tr_offset(int lane, int mbd, int u) {
+  using C = BwdCfg<D>;
+  const int h = lane >> 5, j = lane & 15, dh = (lane >> 4) & 1;
+  const int row = 8 * u + 4 * h + j / 4;
+  const int d0 = 32 * mbd + 16 * dh + 4 * (j & 3);
+  return row * C::ROWB + 16 * ((d0 >> 3) ^ swz_kv<D>(row)) + 2 * (d0 & 7);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t* base, const int (&off)[2]) {
+  const s16x4 lo = lds_read_tr16(base + off[0]);
+  const s16x4 hi = lds_read_tr16(base + off[1]);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ float dot8_f32(u32x4 a, u32x4 b) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = fmaf(bf16lo_to_f32(a[i]), bf16lo_to_f32(b[i]), s);
+    s = fmaf(bf16hi_to_f32(a[i]), bf16hi_to_f32(b[i]), s);
+  }
+  return s;
+}
+
+// Stores a 32 (d) x 32 (rows) fp32 MFMA accumulator block, times `mul`, as bf16 into row `row` (this
+// lane's column) of a row-major [., D] tensor: elements 8g + 4h + 0..3 of the block are contiguous in d.
+template <int D>
+__device__ __forceinline__ void store_rowT(uint16_t* rowp, const f32x16 (&acc)[D / 32], float mul, int h) {
+#pragma unroll
+  for (int mbd = 0; mbd < D / 32; ++mbd)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      u32x2 val;
+      val[0] = pack_bf16x2(acc[mbd][4 * g4 + 0] * mul, acc[mbd][4 * g4 + 1] * mul);
+      val[1] = pack_bf16x2(acc[mbd][4 * g4 + 2] * mul, acc[mbd][4 * g4 + 3] * mul);
+      *reinterpret_cast<u32x2*>(rowp + mbd * 32 + 8 * g4 + 4 * h) = val;
+    }
+}
+
+// ------------------------------------------------------------------------------------------- dQ (and D)
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lk0[C::TKV], lv0[C::TKV], lk1[C::TKV], lv1[C::TKV];
+  auto kbuf = [&](int st) -> uint8_t* { return st == 0 ? lk0 : lk1; };
+  auto vbuf = [&](int st) -> uint8_t* { return st == 0 ? lv0 : lv1; };
+
+  const int lid = xcd_logical_id(blockIdx.x, p.total_q);
+  const int bh = lid / p.n_qt;
+  int qt = lid - bh * p.n_qt;
+  if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query blocks first
+  const int q0 = qt * C::BR;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const size_t head_q = (size_t)bh * p.Nq * D, head_kv = (size_t)bh * p.Nkv * D;
+  const uint16_t* __restrict__ kg = p.k + head_kv;
+  const uint16_t* __restrict__ vg = p.v + head_kv;
+  const int qw0 = q0 + 32 * w, qi = qw0 + l32;
+  const bool row_ok = qi < p.Nq;
+
+  // Q^T and dO^T fragments of this lane's query (d = 16 ks + 8 h .. +7), D_i = dO_i . O_i, LSE_i log2 e
+  bf16x8 qf[C::KS], dof[C::KS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, b = a, o = a;
+    if (row_ok) {
+      const size_t e = head_q + (size_t)qi * D + ks * 16 + 8 * h;
+      a = load16(p.q + e);
+      b = load16(p.dout + e);
+      o = load16(p.o + e);
+    }
+    qf[ks] = __builtin_bit_cast(bf16x8, a);
+    dof[ks] = __builtin_bit_cast(bf16x8, b);
+    dpart += dot8_f32(b, o);
+  }
+  const float Di = pair_sum(dpart);
+  if (row_ok && h == 0) p.delta[(size_t)bh * p.Nq + qi] = Di;
+  const float lse2 = row_ok ? p.lse[(size_t)bh * p.Nq + qi] * kLog2e : 0.f;
+  const float c = p.c;
+
+  int kv_end = p.Nkv;
+  if (CAUSAL) kv_end = min(p.Nkv, q0 + C::BR + p.off);
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  const int wave_kv_end = qw0 >= p.Nq ? 0 : (CAUSAL ? min(p.Nkv, qw0 + 32 + p.off) : p.Nkv);
+  const int lim = CAUSAL ? min(p.Nkv - 1, qi + p.off) : p.Nkv - 1;
+
+  f32x16 acc[C::MBD];
+#pragma unroll
+  for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
+
+  int ld_off[C::LPT_KV];
+#pragma unroll
+  for (int i = 0; i < C::LPT_KV; ++i) {
+    const int r = C::RPL * (w * C::LPT_KV + i) + lane / C::CH, pc = lane % C::CH;
+    ld_off[i] = r * C::ROWB + 16 * (pc ^ swz_kv<D>(r));
+  }
+  auto load_tile = [&](int t, int stage) {
+    const int kv0 = t * C::BC;
+    const int bytes = (p.Nkv - kv0) * C::ROWB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
+#pragma unroll
+    for (int i = 0; i < C::LPT_KV; ++i) {
+      const int blk = 1024 * (w * C::LPT_KV + i);
+      load_lds16(rk, ld_off[i], kbuf(stage) + blk);
+      load_lds16(rv, ld_off[i], vbuf(stage) + blk);
+    }
+  };
+  int row_off[C::KS];  // row l32 of a 32-row block, logical chunk 2 ks + h
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) row_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_kv<D>(l32));
+  int trk[C::MBD][2];
+#pragma unroll
+  for (int mbd = 0; mbd < C::MBD; ++mbd) {
+    trk[mbd][0] = tr_offset<D>(lane, mbd, 0);
+    trk[mbd][1] = tr_offset<D>(lane, mbd, 1);
+  }
+
+  auto compute_tile = [&](const uint8_t* kb, const uint8_t* vb, bool masked, int kv0, auto&& next) {
+    f32x16 S[C::NBLK], dP[C::NBLK];
+#pragma unroll
+    for (int mb = 0; mb < C::NBLK; ++mb) S[mb] = dP[mb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < C::NBLK; ++mb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + row_off[ks] + mb * 32 * C::ROWB);
+        S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb + row_off[ks] + mb * 32 * C::ROWB);
+        dP[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[ks], dP[mb], 0, 0, 0);
+      }
+    next();
+    // dS^T = P^T (dP^T - D), P^T = 2^(s c - LSE log2 e); masked keys get P = 0
+    const int rel = lim - kv0 - 4 * h;
+    bf16x8 dsf[2 * C::NBLK];
+#pragma unroll
+    for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
+      float ds[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * (kc & 1) + i, mb = kc >> 1;
+        float pr = exp2_hw(fmaf(S[mb][r], c, -lse2));
+        if (masked && 32 * mb + 8 * (r >> 2) + (r & 3) > rel) pr = 0.f;
+        ds[i] = pr * (dP[mb][r] - Di);
+      }
+      u32x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+      dsf[kc] = __builtin_bit_cast(bf16x8, pk);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kc = 0; kc < 2 * C::NBLK; ++kc)
+#pragma unroll
+      for (int mbd = 0; mbd < C::MBD; ++mbd)
+        acc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kb + 16 * kc * C::ROWB, trk[mbd]), dsf[kc],
+                                                           acc[mbd], 0, 0, 0);
+  };
+
+  auto tile = [&](auto stage_tag, int t) {
+    constexpr int STAGE = decltype(stage_tag)::value;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const bool more = t + 1 < n_tiles;
+    auto next = [&]() {
+      if (more) load_tile(t + 1, STAGE ^ 1);
+    };
+    const int kv0 = t * C::BC;
+    if (kv0 < wave_kv_end)
+      compute_tile(kbuf(STAGE), vbuf(STAGE), (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off),
+                   kv0, next);
+    else if (more)
+      load_tile(t + 1, STAGE ^ 1);
+  };
+
+  load_tile(0, 0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, t + 1);
+  }
+  if (row_ok) store_rowT<D>(p.dq + head_q + (size_t)qi * D, acc, p.scale, h);
+}
+
+// ----------------------------------------------------------------------------------------------- dK, dV
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lq0[C::TQ], ldo0[C::TQ], lq1[C::TQ], ldo1[C::TQ];
+  __shared__ __attribute__((aligned(16))) float ll0[C::BQ], ld0[C::BQ], ll1[C::BQ], ld1[C::BQ];
+  auto qbuf = [&](int st) -> uint8_t* { return st == 0 ? lq0 : lq1; };
+  auto obuf = [&](int st) -> uint8_t* { return st == 0 ? ldo0 : ldo1; };
+  auto lbuf = [&](int st) -> float* { return st == 0 ? ll0 : ll1; };
+  auto dbuf = [&](int st) -> float* { return st == 0 ? ld0 : ld1; };
+
+  const int lid = xcd_logical_id(blockIdx.x, p.total_k);
+  const int bh = lid / p.n_kt;
+  const int kt = lid - bh * p.n_kt;  // causal: the first key blocks see the most queries
+  const int k0 = kt * C::BR;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const size_t head_q = (size_t)bh * p.Nq * D, head_kv = (size_t)bh * p.Nkv * D;
+  const uint16_t* __restrict__ qg = p.q + head_q;
+  const uint16_t* __restrict__ dog = p.dout + head_q;
+  const int kw0 = k0 + 32 * w, kj = kw0 + l32;
+  const bool key_ok = kj < p.Nkv;
+
+  // K^T and V^T fragments (B operands) of this lane's key
+  bf16x8 kf[C::KS], vf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, b = a;
+    if (key_ok) {
+      const size_t e = head_kv + (size_t)kj * D + ks * 16 + 8 * h;
+      a = load16(p.k + e);
+      b = load16(p.v + e);
+    }
+    kf[ks] = __builtin_bit_cast(bf16x8, a);
+    vf[ks] = __builtin_bit_cast(bf16x8, b);
+  }
+  const float c = p.c;
+
+  // query tiles: causal blocks start at the first query that may see key k0
+  const int n_qtiles = (p.Nq + C::BQ - 1) / C::BQ;
+  const int t0 = CAUSAL ? max(0, k0 - p.off) / C::BQ : 0;
+  const int wave_q_first = kw0 >= p.Nkv ? p.Nq : (CAUSAL ? max(0, kw0 - p.off) : 0);
+
+  f32x16 dka[C::MBD], dva[C::MBD];
+#pragma unroll
+  for (int mbd = 0; mbd < C::MBD; ++mbd) dka[mbd] = dva[mbd] = f32x16{};
+
+  int ld_off[C::LPT_Q];
+#pragma unroll
+  for (int i = 0; i < C::LPT_Q; ++i) {
+    const int r = C::RPL * (w * C::LPT_Q + i) + lane / C::CH, pc = lane % C::CH;
+    ld_off[i] = r * C::ROWB + 16 * (pc ^ swz_kv<D>(r));
+  }
+  auto load_tile = [&](int t, int stage) {
+    const int qr0 = t * C::BQ;
+    const int bytes = (p.Nq - qr0) * C::ROWB;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + (size_t)qr0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dog + (size_t)qr0 * D, bytes);
+#pragma unroll
+    for (int i = 0; i < C::LPT_Q; ++i) {
+      const int blk = 1024 * (w * C::LPT_Q + i);
+      load_lds16(rq, ld_off[i], qbuf(stage) + blk);
+      load_lds16(ro, ld_off[i], obuf(stage) + blk);
+    }
+    if (w == 0 && lane < C::BQ / 4) {  // LSE and D of the tile's queries (zeros past N_q)
+      const size_t e = (size_t)bh * p.Nq + qr0;
+      load_lds16(make_rsrc(p.lse + e, (p.Nq - qr0) * 4), 16 * lane, lbuf(stage));
+      load_lds16(make_rsrc(p.delta + e, (p.Nq - qr0) * 4), 16 * lane, dbuf(stage));
+    }
+  };
+  int row_off[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) row_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_kv<D>(l32));
+  int trq[C::MBD][2];
+#pragma unroll
+  for (int mbd = 0; mbd < C::MBD; ++mbd) {
+    trq[mbd][0] = tr_offset<D>(lane, mbd, 0);
+    trq[mbd][1] = tr_offset<D>(lane, mbd, 1);
+  }
+
+  // one 32-query tile: C rows are queries qr0 + 8 g + 4 h + (r & 3), g = r / 4; the lane's column is key kj
+  auto compute_tile = [&](int st, bool masked, int qr0, auto&& next) {
+    const uint8_t* qb = qbuf(st);
+    const uint8_t* ob = obuf(st);
+    f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + row_off[ks]);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
+      const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ob + row_off[ks]);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dP, 0, 0, 0);
+    }
+    next();
+    const float* lt = lbuf(st);
+    const float* dt = dbuf(st);
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      float pv[8], ds[8];
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int g = 2 * kc + g2;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + 8 * g + 4 * h);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + 8 * g + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float pr = exp2_hw(fmaf(S[r], c, -l4[e] * kLog2e));
+          if (masked && kj > qr0 + 8 * g + 4 * h + e + p.off) pr = 0.f;
+          pv[4 * g2 + e] = pr;
+          ds[4 * g2 + e] = pr * (dP[r] - d4[e]);
+        }
+      }
+      u32x4 pk, dk4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
+        dk4[i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+      }
+      pf[kc] = __builtin_bit_cast(bf16x8, pk);
+      dsf[kc] = __builtin_bit_cast(bf16x8, dk4);
+    }
+    // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int mbd = 0; mbd < C::MBD; ++mbd) {
+        dva[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ob + 16 * kc * C::ROWB, trq[mbd]), pf[kc],
+                                                           dva[mbd], 0, 0, 0);
+        dka[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qb + 16 * kc * C::ROWB, trq[mbd]), dsf[kc],
+                                                           dka[mbd], 0, 0, 0);
+      }
+  };
+
+  auto tile = [&](auto stage_tag, int t) {
+    constexpr int STAGE = decltype(stage_tag)::value;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const bool more = t + 1 < n_qtiles;
+    auto next = [&]() {
+      if (more) load_tile(t + 1, STAGE ^ 1);
+    };
+    const int qr0 = t * C::BQ;
+    if (qr0 + C::BQ - 1 >= wave_q_first)
+      compute_tile(STAGE, CAUSAL && qr0 < kw0 + 31 - p.off, qr0, next);
+    else if (more)
+      load_tile(t + 1, STAGE ^ 1);
+  };
+
+  if (t0 < n_qtiles) load_tile(t0, 0);
+  for (int t = t0; t < n_qtiles; t += 2) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_qtiles) tile(std::integral_constant<int, 1>{}, t + 1);
+  }
+  if (key_ok) {
+    store_rowT<D>(p.dk + head_kv + (size_t)kj * D, dka, p.scale, h);
+    store_rowT<D>(p.dv + head_kv + (size_t)kj * D, dva, 1.f, h);
+  }
+}
+
+// ------------------------------------------------------------------------------------------------ launch
+
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
+  using C = BwdCfg<D>;
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<const uint16_t*>(a.o);
+  p.dout = static_cast<const uint16_t*>(a.dout);
+  p.lse = a.lse;
+  p.delta = a.delta;
+  p.dq = static_cast<uint16_t*>(a.dq);
+  p.dk = static_cast<uint16_t*>(a.dk);
+  p.dv = static_cast<uint16_t*>(a.dv);
+  p.Nq = a.Nq;
+  p.Nkv = a.Nkv;
+  p.off = a.Nkv - a.Nq;
+  p.n_qt = (a.Nq + C::BR - 1) / C::BR;
+  p.n_kt = (a.Nkv + C::BR - 1) / C::BR;
+  p.total_q = a.B * a.H * p.n_qt;
+  p.total_k = a.B * a.H * p.n_kt;
+  p.c = a.scale * kLog2e;
+  p.scale = a.scale;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(p.total_q), dim3(C::NT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.total_k), dim3(C::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+int64_t bwd_bf16_grid(int B, int H, int Nq, int Nkv) {
+  const int64_t bh = (int64_t)B * H;
+  const int64_t a = bh * ((Nq + 127) / 128), b = bh * ((Nkv + 127) / 128);
+  return a > b ? a : b;
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 128) return a.causal ? launch_bwd_d<128, true>(a, s) : launch_bwd_d<128, false>(a, s);
+  return a.causal ? launch_bwd_d<64, true>(a, s) : launch_bwd_d<64, false>(a, s);
+}
+
+}  // namespace fa

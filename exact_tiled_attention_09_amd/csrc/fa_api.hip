@@ -252,6 +252,54 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
   return fa_decode_combine(workspace, workspace_bytes, o, lse, B, H, d, S, stream, dtype);
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int N_q) {
+  int64_t n;
+  if (B < 1 || H < 1 || N_q < 1 || !mul_ok(n, {B, H, N_q, 4}) || n > kMaxElems) return 0;
+  return (size_t)n;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, int B, int H, int N_q, int N_kv, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream, fa_dtype dtype) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+    return fail(FA_ERR_INVALID_ARG, "tensors must be 16-byte aligned (lse 4-byte)");
+  if (B < 1 || H < 1 || N_q < 1 || N_kv < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H, N_q, N_kv must be >= 1 (got %d, %d, %d, %d)", B, H, N_q, N_kv);
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head size d=%d is not built (supported: 64, 128)", d);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  if (causal && N_q > N_kv)
+    return fail(FA_ERR_INVALID_ARG, "causal attention needs N_q <= N_kv (got N_q=%d, N_kv=%d)", N_q, N_kv);
+  if (dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "the backward is built for bf16 only");
+  int64_t nq_el, nkv_el;
+  if (!mul_ok(nq_el, {B, H, N_q, d}) || !mul_ok(nkv_el, {B, H, N_kv, d}) || nq_el > kMaxElems || nkv_el > kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
+  if ((int64_t)N_kv * d * 2 > INT_MAX || (int64_t)N_q * d * 2 > INT_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "the backward supports N * d * 2 <= 2^31 - 1 bytes per head");
+  if (fa::bwd_bf16_grid(B, H, N_q, N_kv) > INT_MAX) return fail(FA_ERR_INVALID_ARG, "launch grid too large");
+  const size_t need = fa_bwd_workspace_bytes(B, H, N_q);
+  fa_status st = check_workspace(workspace, workspace_bytes, need);
+  if (st != FA_OK) return st;
+  const Range rq = span(q, nq_el * 2), rk = span(k, nkv_el * 2), rv = span(v, nkv_el * 2), ro = span(o, nq_el * 2),
+              rdo = span(dout, nq_el * 2), rl = span(lse, (size_t)B * H * N_q * 4), rw = span(workspace, need);
+  const Range outs[4] = {span(dq, nq_el * 2), span(dk, nkv_el * 2), span(dv, nkv_el * 2), rw};
+  const Range ins[6] = {rq, rk, rv, ro, rdo, rl};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], ins[j])) return fail(FA_ERR_INVALID_ARG, "an output or the workspace overlaps an input");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(FA_ERR_INVALID_ARG, "outputs / workspace overlap each other");
+  }
+  fa::BwdArgs a{q, k, v, o, dout, lse, static_cast<float*>(workspace), dq, dk, dv, B, H, N_q, N_kv, d, scale,
+                causal != 0};
+  (void)hipGetLastError();
+  return device_status(fa::launch_bwd_bf16(a, (hipStream_t)stream), "fa_bwd launch");
+}
+
 const char* fa_status_str(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK";

@@ -37,14 +37,32 @@ struct CombineArgs {
   int B, H, d, splits;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;  // workspace [B,H,N_q]
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, Nq, Nkv, d;
+  float scale;
+  bool causal;
+};
+
 // Each launcher assumes validated arguments and returns the launch status.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_split_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_combine_bf16(const CombineArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 
 // Grid-size helpers shared with argument validation.
 int64_t prefill_bf16_grid(int B, int H, int Nq, int d);
 int64_t prefill_f32_grid(int B, int H, int Nq, int d);
+int64_t bwd_bf16_grid(int B, int H, int Nq, int Nkv);
 
 }  // namespace fa

@@ -125,6 +125,35 @@ fa_status fa_decode_split(const void* q, const void* k, const void* v, int B, in
 fa_status fa_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse, int B, int H,
                             int d, int num_splits, void* stream, fa_dtype dtype);
 
+/*
+ * fa_bwd -- gradients of fa_fwd: given the forward's inputs, its output o and
+ * log-sum-exp lse, and the upstream gradient dout = dL/dO, writes
+ * dq = dL/dQ, dk = dL/dK, dv = dL/dV.
+ *
+ * q, o, dout, dq [B,H,N_q,d]; k, v, dk, dv [B,H,N_kv,d]; all bf16, row-major,
+ * 16-byte aligned; lse [B,H,N_q] float32 exactly as fa_fwd wrote it (natural
+ * log, scale included).  scale and causal must be the forward's.
+ * The probabilities are recomputed from q, k and lse rather than stored
+ * (passage: the training section, "More Efficient Backpropagation", of
+ * "FlashAttention Explained: How AI Models Process Attention Faster and Use
+ * Less Memory"; "Recompute probabilities for training" in the contents of "How
+ * FlashAttention Speeds Up LLM Attention").  With P = softmax(scale q k^T):
+ *   dv = P^T dout,  dP = dout v^T,  dS = P * (dP - rowsum(dout * o)),
+ *   dq = scale dS k,  dk = scale dS^T q;
+ * fp32 accumulation, outputs rounded to bf16 to nearest-even.
+ * workspace: caller-owned, >= fa_bwd_workspace_bytes(B, H, N_q) bytes, 16-byte
+ * aligned; it receives rowsum(dout * o) as float32 [B,H,N_q].
+ * Outputs must not overlap inputs, each other or the workspace.  dtype must be
+ * FA_DTYPE_BF16 (FA_DTYPE_F32 returns FA_ERR_UNSUPPORTED); d in {64, 128};
+ * causal needs N_q <= N_kv (bottom-right alignment, as fa_fwd).  Two kernels are
+ * enqueued on `stream`; every output element is summed in a fixed order, so
+ * results are bitwise reproducible.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N_q);
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, int B, int H, int N_q, int N_kv, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream, fa_dtype dtype);
+
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_str(fa_status s);
 

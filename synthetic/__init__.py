@@ -7,7 +7,7 @@ both consume its output without sharing any of the method's code.
 Recipe (one independent stream per tensor slice):
   * every (tensor, b, h) slice of shape [N, d] gets its own PCG64 generator,
     seeded with ``SeedSequence([seed, tensor_id, b, h])`` (tensor_id: q=0, k=1,
-    v=2);
+    v=2, and do=3 for the upstream gradient of the backward pass, N(0,1));
   * the slice is drawn as float32 in C order: ``standard_normal`` for N(0,1),
     ``2*random()-1`` for U(-1,1), and ``4*standard_normal`` for the scaled
     queries of the peaked-softmax workload (scaling by a power of two is exact);
@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-TENSOR_ID = {"q": 0, "k": 1, "v": 2}
+TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3}  # "do": upstream gradient of O (backward pass)
 
 
 @dataclass(frozen=True)
@@ -48,7 +48,7 @@ class Workload:
     num_splits: int = 0
 
     def shape(self, t: str):
-        n = self.Nq if t == "q" else self.Nkv
+        n = self.Nq if t in ("q", "do") else self.Nkv
         return (self.B, self.H, n, self.d)
 
     @property
@@ -147,7 +147,7 @@ def make_tensor(w: Workload, t: str, bh=None, workers: int | None = None) -> np.
     [len(bh), N, d].
     """
     B, H, n, d = w.shape(t)
-    dist = w.dist[t]
+    dist = w.dist.get(t, "normal")
     pairs = [(b, h) for b in range(B) for h in range(H)] if bh is None else list(bh)
     out_dtype = np.float32 if w.dtype == "f32" else np.uint16
     out = np.empty((len(pairs), n, d), dtype=out_dtype)
