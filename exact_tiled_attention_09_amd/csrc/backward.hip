@@ -14,9 +14,10 @@
 //    with a lane pair per query).  It also computes D from dO and O and stores it for the next kernel.
 //    Per 64-key tile: S^T = K Q^T and dP^T = V dO^T (K, V fragments from LDS), dS^T in registers,
 //    dQ^T += K^T dS^T (K^T through ds_read_b64_tr_b16 of the same K tile).
-//  * bwd_dkdv_kernel: one work-group per (b, h, 128 keys), the same layout with the roles of queries and
-//    keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query tile streamed through LDS:
-//    S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through transposing reads).
+//  * bwd_dkdv_kernel (two passes, dV then dK): one work-group per (b, h, 128 keys), the same layout with
+//    the roles of queries and keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query tile
+//    streamed through LDS: S = Q K^T, then dV^T += dO^T P; or S, dP = dO V^T and dK^T += Q^T dS (dO^T,
+//    Q^T through transposing reads).
 // Tiles read both row-wise (ds_read_b128) and transposed (ds_read_b64_tr_b16) use a swizzle that keeps
 // both access patterns on distinct banks.
 #include "common.h"
@@ -257,11 +258,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------------------------------------- dK, dV
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+// One kernel body for dV (WANT_DK = false: S, P, dV^T += dO^T P) and dK (WANT_DK = true: S, dP, dS,
+// dK^T += Q^T dS).  Computing them in two passes recomputes S once more but keeps each pass within the
+// register budget of two waves per SIMD (one fused pass needs both 32x128 accumulators, the K and V
+// fragments and both score tiles at once, and spills).
+template <int D, bool CAUSAL, bool WANT_DK>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t lq0[C::TQ], ldo0[C::TQ], lq1[C::TQ], ldo1[C::TQ];
   __shared__ __attribute__((aligned(16))) float ll0[C::BQ], ld0[C::BQ], ll1[C::BQ], ld1[C::BQ];
+  // V of the work-group's 128 keys (B operand of dP = dO V^T; dK pass only)
+  __shared__ __attribute__((aligned(16))) uint8_t lvk[WANT_DK ? C::BR * C::ROWB : 16];
   auto qbuf = [&](int st) -> uint8_t* { return st == 0 ? lq0 : lq1; };
   auto obuf = [&](int st) -> uint8_t* { return st == 0 ? ldo0 : ldo1; };
   auto lbuf = [&](int st) -> float* { return st == 0 ? ll0 : ll1; };
@@ -279,19 +286,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int kw0 = k0 + 32 * w, kj = kw0 + l32;
   const bool key_ok = kj < p.Nkv;
 
-  // K^T and V^T fragments (B operands) of this lane's key
-  bf16x8 kf[C::KS], vf[C::KS];
+  // K^T fragments (B operand of S = Q K^T) of this lane's key
+  bf16x8 kf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = a;
-    if (key_ok) {
-      const size_t e = head_kv + (size_t)kj * D + ks * 16 + 8 * h;
-      a = load16(p.k + e);
-      b = load16(p.v + e);
-    }
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (key_ok) a = load16(p.k + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
     kf[ks] = __builtin_bit_cast(bf16x8, a);
-    vf[ks] = __builtin_bit_cast(bf16x8, b);
   }
+  if (WANT_DK) {  // the block's V rows into LDS (rows past N_kv read zeros); visible after the first barrier
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_kv + (size_t)k0 * D, (p.Nkv - k0) * C::ROWB);
+    constexpr int LPV = C::BR * C::ROWB / (C::NT * 16);
+#pragma unroll
+    for (int i = 0; i < LPV; ++i) {
+      const int r = C::RPL * (w * LPV + i) + lane / C::CH, pc = lane % C::CH;
+      load_lds16(rv, r * C::ROWB + 16 * (pc ^ swz_kv<D>(r)), lvk + 1024 * (w * LPV + i));
+    }
+  }
+  const uint8_t* vrow = lvk + 32 * w * C::ROWB;  // this wave's 32 keys
   const float c = p.c;
 
   // query tiles: causal blocks start at the first query that may see key k0
@@ -299,9 +311,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int t0 = CAUSAL ? max(0, k0 - p.off) / C::BQ : 0;
   const int wave_q_first = kw0 >= p.Nkv ? p.Nq : (CAUSAL ? max(0, kw0 - p.off) : 0);
 
-  f32x16 dka[C::MBD], dva[C::MBD];
+  f32x16 acc[C::MBD];
 #pragma unroll
-  for (int mbd = 0; mbd < C::MBD; ++mbd) dka[mbd] = dva[mbd] = f32x16{};
+  for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
 
   int ld_off[C::LPT_Q];
 #pragma unroll
@@ -320,10 +332,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       load_lds16(rq, ld_off[i], qbuf(stage) + blk);
       load_lds16(ro, ld_off[i], obuf(stage) + blk);
     }
-    if (w == 0 && lane < C::BQ / 4) {  // LSE and D of the tile's queries (zeros past N_q)
+    if (w == 0 && lane < C::BQ / 4) {  // LSE (and D) of the tile's queries (zeros past N_q)
       const size_t e = (size_t)bh * p.Nq + qr0;
       load_lds16(make_rsrc(p.lse + e, (p.Nq - qr0) * 4), 16 * lane, lbuf(stage));
-      load_lds16(make_rsrc(p.delta + e, (p.Nq - qr0) * 4), 16 * lane, dbuf(stage));
+      if (WANT_DK) load_lds16(make_rsrc(p.delta + e, (p.Nq - qr0) * 4), 16 * lane, dbuf(stage));
     }
   };
   int row_off[C::KS];
@@ -345,49 +357,46 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     for (int ks = 0; ks < C::KS; ++ks) {
       const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + row_off[ks]);
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
-      const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ob + row_off[ks]);
-      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dP, 0, 0, 0);
+      if (WANT_DK) {
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ob + row_off[ks]);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vrow + row_off[ks]);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dP, 0, 0, 0);
+      }
     }
     next();
     const float* lt = lbuf(st);
     const float* dt = dbuf(st);
-    bf16x8 pf[2], dsf[2];
+    bf16x8 bf[2];  // P (dV pass) or dS (dK pass), packed for the B operand
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      float pv[8], ds[8];
+      float x[8];
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {
         const int g = 2 * kc + g2;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + 8 * g + 4 * h);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + 8 * g + 4 * h);
+        f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+        if (WANT_DK) d4 = *reinterpret_cast<const f32x4*>(dt + 8 * g + 4 * h);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           float pr = exp2_hw(fmaf(S[r], c, -l4[e] * kLog2e));
           if (masked && kj > qr0 + 8 * g + 4 * h + e + p.off) pr = 0.f;
-          pv[4 * g2 + e] = pr;
-          ds[4 * g2 + e] = pr * (dP[r] - d4[e]);
+          x[4 * g2 + e] = WANT_DK ? pr * (dP[r] - d4[e]) : pr;
         }
       }
-      u32x4 pk, dk4;
+      u32x4 pk;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
-        dk4[i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
-      }
-      pf[kc] = __builtin_bit_cast(bf16x8, pk);
-      dsf[kc] = __builtin_bit_cast(bf16x8, dk4);
+      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      bf[kc] = __builtin_bit_cast(bf16x8, pk);
     }
-    // dV^T += dO^T P,  dK^T += Q^T dS
+    // dV^T += dO^T P  or  dK^T += Q^T dS
+    const uint8_t* ab = WANT_DK ? qb : ob;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd) {
-        dva[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ob + 16 * kc * C::ROWB, trq[mbd]), pf[kc],
-                                                           dva[mbd], 0, 0, 0);
-        dka[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qb + 16 * kc * C::ROWB, trq[mbd]), dsf[kc],
-                                                           dka[mbd], 0, 0, 0);
-      }
+      for (int mbd = 0; mbd < C::MBD; ++mbd)
+        acc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ab + 16 * kc * C::ROWB, trq[mbd]), bf[kc],
+                                                           acc[mbd], 0, 0, 0);
   };
 
   auto tile = [&](auto stage_tag, int t) {
@@ -410,9 +419,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     tile(std::integral_constant<int, 0>{}, t);
     if (t + 1 < n_qtiles) tile(std::integral_constant<int, 1>{}, t + 1);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // every load has landed before the work-group ends (no tile: V rows)
   if (key_ok) {
-    store_rowT<D>(p.dk + head_kv + (size_t)kj * D, dka, p.scale, h);
-    store_rowT<D>(p.dv + head_kv + (size_t)kj * D, dva, 1.f, h);
+    if (WANT_DK) store_rowT<D>(p.dk + head_kv + (size_t)kj * D, acc, p.scale, h);
+    else store_rowT<D>(p.dv + head_kv + (size_t)kj * D, acc, 1.f, h);
   }
 }
 
@@ -444,7 +454,10 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(p.total_q), dim3(C::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.total_k), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3(p.total_k), dim3(C::NT), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3(p.total_k), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
