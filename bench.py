@@ -138,6 +138,24 @@ def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int):
                               "frac_of_peak": round(w.flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                               "avg_kernel_ms": round(t, 4)}
     del q, k, v, o, lse
+    # backward of the causal prefill workload (B1 H32 N8192 d128): dQ, dK, dV from O, LSE and dO
+    w = syn.WORKLOADS["c3"]
+    log(f"[bench] next: backward of {w.name}")
+    q, k, v = (upload(syn.make_tensor(w, t), "bf16") for t in "qkv")
+    do = upload(syn.make_tensor(w, "do"), "bf16")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq), dtype=torch.uint8, device=dev)
+    t = time_events(lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, w.scale, True, ws, stream), stream,
+                    max(3, steps // 4), warmup)
+    fl = 2.5 * w.flops  # five products of 2*d flops per allowed pair (S, dP, dV, dQ, dK)
+    out["backward"] = {"workload": "fa_bwd causal bf16 B1 H32 N8192 d128 (dQ, dK, dV)",
+                       "value": round(fl / (t * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                       "flops_per_call": fl, "flops_convention": "2.5x the forward's 4*d per allowed pair",
+                       "frac_of_peak": round(fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "avg_ms": round(t, 4)}
     return out
 
 
