@@ -6,6 +6,7 @@ from .attention import (  # noqa: F401
     combine_ref,
     decode_ref,
     default_scale,
+    gqa_decode_ref,
     merge_partials,
     probabilities_ref,
     split_bounds,

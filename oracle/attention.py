@@ -66,6 +66,7 @@ __all__ = [
     "combine_ref",
     "decode_ref",
     "attention_bwd_ref",
+    "gqa_decode_ref",
 ]
 
 
@@ -246,6 +247,21 @@ def decode_ref(q, k, v, scale: float):
         q = q[:, :, None, :]
     o, lse = attention_ref(q, k, v, scale, False)
     return o[:, :, 0], lse[:, :, 0]
+
+
+def gqa_decode_ref(q, k, v, scale: float):
+    """Decode with grouped key/value heads: q [B,H,d]; k, v [B,H_kv,N_kv,d], H a multiple of H_kv.
+
+    Query head h attends to key/value head h // (H / H_kv) (consecutive query heads share one key/value
+    head).  Written as the plain definition on explicitly repeated keys and values.
+    """
+    q = np.asarray(q, np.float64)
+    k, v = _as4(k), _as4(v)
+    H, H_kv = q.shape[1], k.shape[1]
+    if H % H_kv:
+        raise ValueError("H must be a multiple of H_kv")
+    g = H // H_kv
+    return decode_ref(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), scale)
 
 
 def attention_bwd_ref(q, k, v, do, scale: float, causal: bool):
