@@ -133,11 +133,31 @@ def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
     t = time_events(lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream), stream, steps, warmup)
-    out["chunked_prefill"] = {"workload": "fa_fwd causal (bottom-right) bf16 B1 H32 N_q1000 N_kv8192 d128",
-                              "value": round(w.flops / (t * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                              "frac_of_peak": round(w.flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                              "avg_kernel_ms": round(t, 4)}
-    del q, k, v, o, lse
+    S = 2
+    ws = torch.empty(fa.fa_fwd_split_workspace_bytes(w.B, w.H, w.Nq, w.d, S), dtype=torch.uint8, device=dev)
+    ts = time_events(lambda: fa.fa_fwd_split(q, k, v, o, lse, w.scale, True, S, ws, stream), stream, steps, warmup)
+    out["chunked_prefill"] = {"workload": "causal (bottom-right) bf16 B1 H32 N_q1000 N_kv8192 d128",
+                              "value": round(w.flops / (ts * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                              "frac_of_peak": round(w.flops / (ts * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "entry_point": f"fa_fwd_split, {S} splits + combine", "avg_ms": round(ts, 4),
+                              "fa_fwd_single_pass_tflops": round(w.flops / (t * 1e-3) / 1e12, 2)}
+    del q, k, v, o, lse, ws
+    # grouped key/value decode: 32 query heads over 8 key/value heads, 8192 cached keys
+    B, H, Hkv, N, d, S = 64, 32, 8, 8192, 128, 8
+    wq = syn.custom(B, H, 1, 1, d, "bf16", False, None, seed=6)
+    wkv = syn.custom(B, Hkv, 1, N, d, "bf16", False, None, seed=7)
+    log(f"[bench] next: GQA decode B{B} H{H} H_kv{Hkv} N_kv{N} d{d}")
+    q = upload(syn.make_tensor(wq, "q")[:, :, 0].copy(), "bf16")
+    k, v = upload(syn.make_tensor(wkv, "k"), "bf16"), upload(syn.make_tensor(wkv, "v"), "bf16")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_decode_gqa_workspace_bytes(B, H, Hkv, N, d, S), dtype=torch.uint8, device=dev)
+    t = time_events(lambda: fa.fa_decode_gqa(q, k, v, o, lse, wq.scale, S, ws, stream), stream, steps, warmup)
+    by = 2 * B * Hkv * N * d * 2 + 2 * B * H * d * 2  # K, V read once; q read, o written
+    out["gqa_decode"] = {"workload": f"fa_decode_gqa bf16 B{B} H{H} H_kv{Hkv} N_kv{N} d{d}, {S} splits + combine",
+                         "value": round(by / (t * 1e-3) / 1e9, 1), "unit": "GB/s",
+                         "frac_of_peak": round(by / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "avg_ms": round(t, 4)}
+    del q, k, v, o, lse, ws
     # backward of the causal prefill workload (B1 H32 N8192 d128): dQ, dK, dV from O, LSE and dO
     w = syn.WORKLOADS["c3"]
     log(f"[bench] next: backward of {w.name}")

@@ -51,6 +51,13 @@ def lib() -> ctypes.CDLL:
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp, i]
     L.fa_decode_split.argtypes = [vp, vp, vp, i, i, i, i, f, i, vp, sz, vp, i]
     L.fa_decode_combine.argtypes = [vp, sz, vp, vp, i, i, i, i, vp, i]
+    L.fa_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.fa_fwd_split_workspace_bytes.restype = sz
+    L.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp, i]
+    L.fa_decode_gqa_num_splits.argtypes = [i, i, i, i, i, i]
+    L.fa_decode_gqa_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.fa_decode_gqa_workspace_bytes.restype = sz
+    L.fa_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp, i]
     L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
     L.fa_bwd_workspace_bytes.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp, i]
@@ -60,7 +67,7 @@ def lib() -> ctypes.CDLL:
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = ctypes.c_char_p
     for name in ("fa_fwd", "fa_fwd_bf16", "fa_fwd_f32", "fa_decode", "fa_decode_split", "fa_decode_combine",
-                 "fa_decode_num_splits", "fa_bwd"):
+                 "fa_decode_num_splits", "fa_bwd", "fa_fwd_split", "fa_decode_gqa", "fa_decode_gqa_num_splits"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -174,6 +181,52 @@ def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None):
     _check(st, "fa_decode_combine")
 
 
+def fa_fwd_split_workspace_bytes(B: int, H: int, N_q: int, d: int, num_splits: int) -> int:
+    return lib().fa_fwd_split_workspace_bytes(B, H, N_q, d, num_splits)
+
+
+def fa_fwd_split(q, k, v, o, lse, scale: float, causal: bool, num_splits: int, workspace, stream=None):
+    """libfa fa_fwd_split: fa_fwd with the keys cut into num_splits ranges (bf16); workspace a byte device
+    tensor of at least fa_fwd_split_workspace_bytes()."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    _check_tensor("k", k, (B, H, Nkv, d), q.dtype)
+    _check_tensor("v", v, (B, H, Nkv, d), q.dtype)
+    _check_tensor("o", o, (B, H, Nq, d), q.dtype)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H, Nq), torch.float32)
+    st = lib().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nkv, d, float(scale),
+                            int(bool(causal)), int(num_splits), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream), _dtype_code(q))
+    _check(st, "fa_fwd_split")
+
+
+def fa_decode_gqa_num_splits(B: int, H: int, H_kv: int, N_kv: int, d: int, num_splits: int = 0) -> int:
+    return lib().fa_decode_gqa_num_splits(B, H, H_kv, N_kv, d, num_splits)
+
+
+def fa_decode_gqa_workspace_bytes(B: int, H: int, H_kv: int, N_kv: int, d: int, num_splits: int = 0) -> int:
+    return lib().fa_decode_gqa_workspace_bytes(B, H, H_kv, N_kv, d, num_splits)
+
+
+def fa_decode_gqa(q, k, v, o, lse, scale: float, num_splits: int, workspace, stream=None):
+    """libfa fa_decode_gqa: q [B,H,d], k/v [B,H_kv,N_kv,d] (bf16, H a multiple of H_kv); o [B,H,d];
+    lse [B,H] fp32 or None; workspace of at least fa_decode_gqa_workspace_bytes()."""
+    import torch
+    B, H, d = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    _check_tensor("q", q, (B, H, d), k.dtype)
+    _check_tensor("v", v, (B, Hkv, Nkv, d), k.dtype)
+    _check_tensor("o", o, (B, H, d), k.dtype)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H), torch.float32)
+    st = lib().fa_decode_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nkv, d, float(scale),
+                             int(num_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream), _dtype_code(k))
+    _check(st, "fa_decode_gqa")
+
+
 def fa_bwd_workspace_bytes(B: int, H: int, N_q: int) -> int:
     return lib().fa_bwd_workspace_bytes(B, H, N_q)
 
@@ -238,3 +291,31 @@ def attention_backward(q, k, v, o, lse, dout, scale: float | None = None, causal
     ws = torch.empty(fa_bwd_workspace_bytes(B, H, Nq), dtype=torch.uint8, device=q.device)
     fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, causal, ws, stream)
     return dq, dk, dv
+
+
+def attention_split(q, k, v, num_splits: int, scale: float | None = None, causal: bool = False, stream=None):
+    """Allocate o, lse and the workspace and run fa_fwd_split; returns (o, lse)."""
+    import torch
+    B, H, Nq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    ws = torch.empty(fa_fwd_split_workspace_bytes(B, H, Nq, d, num_splits), dtype=torch.uint8, device=q.device)
+    fa_fwd_split(q, k, v, o, lse, scale, causal, num_splits, ws, stream)
+    return o, lse
+
+
+def decode_gqa(q, k, v, scale: float | None = None, num_splits: int = 0, stream=None):
+    """Allocate o, lse and the workspace and run fa_decode_gqa; returns (o, lse)."""
+    import torch
+    B, H, d = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    n = fa_decode_gqa_workspace_bytes(B, H, Hkv, Nkv, d, num_splits)
+    if n == 0:
+        raise FaError(FA_ERR_INVALID_ARG, "fa_decode_gqa_workspace_bytes", last_error())
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    fa_decode_gqa(q, k, v, o, lse, scale, num_splits, ws, stream)
+    return o, lse

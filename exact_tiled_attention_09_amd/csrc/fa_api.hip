@@ -78,7 +78,7 @@ fa_status check_fwd(const void* q, const void* k, const void* v, void* o, float*
   if (dtype == FA_DTYPE_BF16 && (int64_t)N_kv * d * 2 > INT_MAX)
     return fail(FA_ERR_UNSUPPORTED, "bf16 prefill supports N_kv * d * 2 <= 2^31 - 1 bytes per head (got N_kv=%d, d=%d)",
                 N_kv, d);
-  const int64_t grid = dtype == FA_DTYPE_BF16 ? fa::prefill_bf16_grid(B, H, N_q, d) : fa::prefill_f32_grid(B, H, N_q, d);
+  const int64_t grid = dtype == FA_DTYPE_BF16 ? fa::prefill_bf16_grid(B, H, N_q, d, 0) : fa::prefill_f32_grid(B, H, N_q, d);
   if (grid > INT_MAX) return fail(FA_ERR_INVALID_ARG, "launch grid too large (%lld work-groups)", (long long)grid);
   const Range rq = span(q, nq_el * *esz), rk = span(k, nkv_el * *esz), rv = span(v, nkv_el * *esz);
   const Range ro = span(o, nq_el * *esz);
@@ -250,6 +250,69 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
   st = fa_decode_split(q, k, v, B, H, N_kv, d, scale, S, workspace, workspace_bytes, stream, dtype);
   if (st != FA_OK) return st;
   return fa_decode_combine(workspace, workspace_bytes, o, lse, B, H, d, S, stream, dtype);
+}
+
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N_q, int d, int num_splits) {
+  int64_t n;
+  if (B < 1 || H < 1 || N_q < 1 || num_splits < 1 || (d != 64 && d != 128) ||
+      !mul_ok(n, {B, H, N_q, num_splits, d + 1, 4}) || n > kMaxElems)
+    return 0;
+  return (size_t)n;
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
+                       int N_kv, int d, float scale, int causal, int num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream, fa_dtype dtype) {
+  size_t esz = 0;
+  fa_status st = check_fwd(q, k, v, o, lse, B, H, N_q, N_kv, d, scale, causal, dtype, &esz);
+  if (st != FA_OK) return st;
+  if (dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "the split-KV forward is built for bf16 only");
+  if (num_splits < 1 || num_splits > N_kv)
+    return fail(FA_ERR_INVALID_ARG, "num_splits must be in [1, N_kv] (got %d)", num_splits);
+  if (fa::prefill_bf16_grid(B, H, N_q, d, num_splits) > INT_MAX ||
+      (int64_t)B * H * N_q > INT_MAX)
+    return fail(FA_ERR_INVALID_ARG, "launch grid too large");
+  const size_t need = fa_fwd_split_workspace_bytes(B, H, N_q, d, num_splits);
+  if (need == 0) return fail(FA_ERR_INVALID_ARG, "workspace size overflows");
+  st = check_workspace(workspace, workspace_bytes, need);
+  if (st != FA_OK) return st;
+  const size_t nq_b = (size_t)B * H * N_q * d * 2, nkv_b = (size_t)B * H * N_kv * d * 2;
+  const Range rw = span(workspace, need);
+  if (overlap(rw, span(q, nq_b)) || overlap(rw, span(k, nkv_b)) || overlap(rw, span(v, nkv_b)) ||
+      overlap(rw, span(o, nq_b)) || (lse && overlap(rw, span(lse, (size_t)B * H * N_q * 4))))
+    return fail(FA_ERR_INVALID_ARG, "workspace overlaps a tensor");
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = ws_o + (size_t)B * H * N_q * num_splits * d;
+  fa::PrefillArgs a{q, k, v, o, lse, B, H, N_q, N_kv, d, scale, causal != 0, num_splits, ws_o, ws_lse};
+  (void)hipGetLastError();
+  hipError_t e = fa::launch_prefill_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return device_status(e, "fa_fwd_split launch");
+  fa::CombineArgs cmb{ws_o, ws_lse, o, lse, B * H * N_q, 1, d, num_splits};
+  return device_status(fa::launch_decode_combine_bf16(cmb, (hipStream_t)stream), "fa_fwd_split combine launch");
+}
+
+int fa_decode_gqa_num_splits(int B, int H, int H_kv, int N_kv, int d, int num_splits) {
+  if (H_kv < 1 || H < H_kv || H % H_kv != 0) return 0;
+  return fa_decode_num_splits(B, H_kv, N_kv, d, num_splits);
+}
+
+size_t fa_decode_gqa_workspace_bytes(int B, int H, int H_kv, int N_kv, int d, int num_splits) {
+  const int S = fa_decode_gqa_num_splits(B, H, H_kv, N_kv, d, num_splits);
+  if (S < 1) return 0;
+  return fa_fwd_split_workspace_bytes(B, H_kv, H / H_kv, d, S);
+}
+
+fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                        int N_kv, int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                        void* stream, fa_dtype dtype) {
+  if (H_kv < 1 || H < 1 || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "H must be a positive multiple of H_kv (got H=%d, H_kv=%d)", H, H_kv);
+  int S = 0;
+  fa_status st = check_decode_sizes(B, H_kv, N_kv, d, num_splits, &S);
+  if (st != FA_OK) return st;
+  // the G = H / H_kv query heads of a key/value head are the query rows of one forward over its cache
+  return fa_fwd_split(q, k, v, o, lse, B, H_kv, H / H_kv, N_kv, d, scale, 0, S, workspace, workspace_bytes, stream,
+                      dtype);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N_q) {

@@ -16,6 +16,10 @@ struct PrefillArgs {
   int B, H, Nq, Nkv, d;
   float scale;
   bool causal;
+  // split-KV forward (bf16): splits > 0 writes per-range partials instead of o / lse
+  int splits = 0;
+  float* ws_o = nullptr;    // [B*H*N_q, splits, d]
+  float* ws_lse = nullptr;  // [B*H*N_q, splits]
 };
 
 struct DecodeArgs {
@@ -61,7 +65,8 @@ hipError_t launch_decode_combine_bf16(const CombineArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 
 // Grid-size helpers shared with argument validation.
-int64_t prefill_bf16_grid(int B, int H, int Nq, int d);
+int64_t prefill_bf16_grid(int B, int H, int Nq, int d, int splits = 0);
+int prefill_split_tiles(int Nkv, int S);  // 64-key tiles per split of the split-KV forward
 int64_t prefill_f32_grid(int B, int H, int Nq, int d);
 int64_t bwd_bf16_grid(int B, int H, int Nq, int Nkv);
 

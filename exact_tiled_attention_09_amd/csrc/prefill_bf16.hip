@@ -51,6 +51,10 @@ struct PrefillParams {
   int Nq, Nkv, off, n_qt, total;
   float c;        // max(|scale| * log2(e), 2^-126): strictly positive so masked -inf scores give 2^-inf = 0
   uint32_t qxor;  // 0x80008000 when scale < 0: q is negated on load (exact) so that c > 0
+  // split-KV mode: key tiles [s*split_tiles, (s+1)*split_tiles) per work-group, partials into the workspace
+  int S, split_tiles;
+  float* __restrict__ ws_o;    // [B*H*N_q, S, D] fp32, O_s normalised
+  float* __restrict__ ws_lse;  // [B*H*N_q, S] fp32, natural log; -inf for a row with no key in the range
 };
 
 #ifndef FA_NW
@@ -95,7 +99,7 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
   return acc;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(PrefillParams p) {
   using C = Cfg<D>;
   // One LDS array per stage and operand: the compiler can then tell that the direct loads into one
@@ -105,8 +109,13 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
   auto vbuf = [&](int st) -> uint8_t* { return st == 0 ? lds_v0 : lds_v1; };
 
   const int lid = xcd_logical_id(blockIdx.x, p.total);
-  const int bh = lid / p.n_qt;
-  int qt = lid - bh * p.n_qt;
+  const int per_bh = SPLIT ? p.n_qt * p.S : p.n_qt;
+  const int bh = lid / per_bh;
+  int qt = lid - bh * per_bh, split = 0;
+  if (SPLIT) {
+    split = qt % p.S;
+    qt /= p.S;
+  }
   if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
   const int q0 = qt * C::BR;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -132,7 +141,11 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
 
   int kv_end = p.Nkv;
   if (CAUSAL) kv_end = min(p.Nkv, q0 + C::BR + p.off);
-  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  int t_beg = 0, n_tiles = (kv_end + C::BC - 1) / C::BC;  // tiles [t_beg, n_tiles) of this work-group
+  if (SPLIT) {
+    t_beg = min(split * p.split_tiles, n_tiles);
+    n_tiles = min(t_beg + p.split_tiles, n_tiles);
+  }
   // keys this wave needs (0 when the wave's rows lie past N_q)
   const int wave_kv_end = qw0 >= p.Nq ? 0 : (CAUSAL ? min(p.Nkv, qw0 + 32 + p.off) : p.Nkv);
   const int lim = CAUSAL ? min(p.Nkv - 1, qi + p.off) : p.Nkv - 1;  // last key this row may attend
@@ -260,7 +273,9 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
       const float mn = fmaxf(m_run, pair_max(mx) * c);
       alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - mn);
       m_run = mn;
-      weights(mn);
+      // a row none of whose keys so far is allowed (possible only inside a key range of a split) keeps
+      // m = -inf and gets zero weights (reference 0 instead of -inf avoids -inf - (-inf))
+      weights(mn == kNegInf ? 0.f : mn);
 #pragma unroll
       for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[mbd] *= alpha;
     }
@@ -300,8 +315,9 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
       load_tile(t + 1, STAGE ^ 1);
   };
 
-  load_tile(0, 0);
-  for (int t = 0; t < n_tiles; t += 2) {
+  // the two stages alternate from the first tile of the range, so stage = (t - t_beg) & 1
+  if (t_beg < n_tiles) load_tile(t_beg, 0);
+  for (int t = t_beg; t < n_tiles; t += 2) {
     tile(std::integral_constant<int, 0>{}, t);
     if (t + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, t + 1);
   }
@@ -310,6 +326,24 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
   // O / l_hat (the weights that entered the value product) rounded to bf16, LSE from the fp32 sum.
   const float lt = pair_sum(l_run);
   const float inv = 1.f / pair_sum(lh_run);
+  if (SPLIT) {  // fp32 partial of this key range; a row with no key in it gets O = 0, LSE = -inf
+    if (qi < p.Nq) {
+      const size_t row = (size_t)bh * p.Nq + qi;
+      const bool any = lt > 0.f;
+      float* orow = p.ws_o + (row * p.S + split) * D;
+#pragma unroll
+      for (int mbd = 0; mbd < C::MBD; ++mbd)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 val;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = any ? oacc[mbd][4 * g4 + e] * inv : 0.f;
+          *reinterpret_cast<f32x4*>(orow + mbd * 32 + 8 * g4 + 4 * h) = val;
+        }
+      if (h == 0) p.ws_lse[row * p.S + split] = any ? (m_run + log2_hw(lt)) * kLn2 : kNegInf;
+    }
+    return;
+  }
   if (qi < p.Nq) {
     uint16_t* orow = p.o + head_q + (size_t)qi * D;
 #pragma unroll
@@ -328,12 +362,12 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
 
 // ---------------------------------------------------------------------------------------------- launch
 
-int64_t prefill_bf16_grid(int B, int H, int Nq, int d) {
+int64_t prefill_bf16_grid(int B, int H, int Nq, int d, int splits) {
   const int br = d == 128 ? Cfg<128>::BR : Cfg<64>::BR;
-  return (int64_t)B * H * ((Nq + br - 1) / br);
+  return (int64_t)B * H * ((Nq + br - 1) / br) * (splits > 0 ? splits : 1);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   using C = Cfg<D>;
   PrefillParams p;
@@ -346,16 +380,29 @@ static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   p.Nkv = a.Nkv;
   p.off = a.Nkv - a.Nq;
   p.n_qt = (a.Nq + C::BR - 1) / C::BR;
-  p.total = a.B * a.H * p.n_qt;
+  p.S = SPLIT ? a.splits : 1;
+  p.split_tiles = prefill_split_tiles(a.Nkv, p.S);
+  p.total = a.B * a.H * p.n_qt * p.S;
   p.c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-126f);
   p.qxor = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3(p.total), dim3(C::NT), 0, s, p);
+  p.ws_o = a.ws_o;
+  p.ws_lse = a.ws_lse;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, SPLIT>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
+int prefill_split_tiles(int Nkv, int S) {
+  const int tiles = (Nkv + Cfg<128>::BC - 1) / Cfg<128>::BC;
+  return (tiles + S - 1) / S;
+}
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-  if (a.d == 128) return a.causal ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
-  return a.causal ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);
+  if (a.splits > 0) {
+    if (a.d == 128) return a.causal ? launch_d<128, true, true>(a, s) : launch_d<128, false, true>(a, s);
+    return a.causal ? launch_d<64, true, true>(a, s) : launch_d<64, false, true>(a, s);
+  }
+  if (a.d == 128) return a.causal ? launch_d<128, true, false>(a, s) : launch_d<128, false, false>(a, s);
+  return a.causal ? launch_d<64, true, false>(a, s) : launch_d<64, false, false>(a, s);
 }
 
 }  // namespace fa

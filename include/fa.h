@@ -126,6 +126,42 @@ fa_status fa_decode_combine(const void* workspace, size_t workspace_bytes, void*
                             int d, int num_splits, void* stream, fa_dtype dtype);
 
 /*
+ * fa_fwd_split -- fa_fwd with the keys of every query tile cut into num_splits
+ * contiguous ranges of 64-key tiles, processed by separate work-groups, and the
+ * per-range partials merged by their log-sum-exp (the combine of fa_decode).
+ * Same result as fa_fwd within rounding; use it when B*H*ceil(N_q/128) is too
+ * small to fill the GPU (a short chunk of queries against a long cache).
+ * Arguments as fa_fwd (bf16 only; FA_DTYPE_F32 returns FA_ERR_UNSUPPORTED),
+ * plus num_splits in [1, N_kv] and a caller-owned workspace of at least
+ * fa_fwd_split_workspace_bytes(B, H, N_q, d, num_splits) bytes, 16-byte aligned:
+ *   float O_s[B*H*N_q][S][d] at byte offset 0, float lse_s[B*H*N_q][S] after it.
+ * Passage: as fa_fwd; the merge is the decode combine of "Where you actually feel
+ * it" ("Flash Attention Explained: Same Maths, Far Less Memory").
+ */
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N_q, int d, int num_splits);
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
+                       int N_kv, int d, float scale, int causal, int num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream, fa_dtype dtype);
+
+/*
+ * fa_decode_gqa -- decode with grouped key/value heads: q [B,H,d] against
+ * k, v [B,H_kv,N_kv,d] where query head h uses key/value head h / (H / H_kv)
+ * (H a multiple of H_kv; H_kv == 1 is multi-query attention).  Writes o [B,H,d]
+ * bf16 and, if lse != NULL, lse [B,H] float32; no mask.  Each key/value head is
+ * read once for all H / H_kv query heads that share it, which is what makes the
+ * KV cache cheaper ("Flash Attention Explained: Same Maths, Far Less Memory",
+ * "Where you actually feel it": the KV cache dominates decode).
+ * num_splits in [0, N_kv] (0 = auto over B*H_kv sequences); the workspace needs
+ * fa_decode_gqa_workspace_bytes(B, H, H_kv, N_kv, d, num_splits) bytes (the
+ * layout of fa_fwd_split with N_q = H / H_kv).  bf16 only.
+ */
+int fa_decode_gqa_num_splits(int B, int H, int H_kv, int N_kv, int d, int num_splits);
+size_t fa_decode_gqa_workspace_bytes(int B, int H, int H_kv, int N_kv, int d, int num_splits);
+fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                        int N_kv, int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                        void* stream, fa_dtype dtype);
+
+/*
  * fa_bwd -- gradients of fa_fwd: given the forward's inputs, its output o and
  * log-sum-exp lse, and the upstream gradient dout = dL/dO, writes
  * dq = dL/dQ, dk = dL/dK, dv = dL/dV.
