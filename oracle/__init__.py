@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     default_scale,
     gqa_decode_ref,
     merge_partials,
+    paged_decode_ref,
     probabilities_ref,
     split_bounds,
     split_partials_ref,
