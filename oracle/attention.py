@@ -269,10 +269,12 @@ def paged_decode_ref(q, k_pages, v_pages, block_table, seq_lens, scale: float):
     """Decode against a paged KV cache (the paging idea of "Paged Attention: Fixing the KV Cache Memory
     Problem", listed among the related posts of "Flash Attention Explained: Speed From Memory Movement").
 
-    k_pages, v_pages: [num_pages, H, P, d]; token t of sequence b lives in page block_table[b, t // P],
-    row t % P.  Sequence b has seq_lens[b] tokens.  A table entry outside [0, num_pages) marks its tokens
-    absent (they take no part).  q [B, H, d] -> (O [B, H, d], LSE [B, H]); a sequence with no token gives
-    O = 0 and LSE = -inf.  Written out: gather each sequence's tokens, then the plain definition.
+    k_pages, v_pages: [num_pages, H_kv, P, d]; token t of sequence b lives in page block_table[b, t // P],
+    row t % P.  Sequence b has seq_lens[b] tokens, taken as min(max(seq_lens[b], 0), max_blocks * P) so
+    that the table is never read past its width.  A table entry outside [0, num_pages) marks its tokens
+    absent (they take no part).  q [B, H, d] with H a multiple of H_kv; query head h reads key/value head
+    h // (H / H_kv).  Returns (O [B, H, d], LSE [B, H]); a sequence with no token gives O = 0 and
+    LSE = -inf.  Written out: gather each sequence's tokens, then the grouped-head decode definition.
     """
     q = np.asarray(q, np.float64)
     kp, vp = np.asarray(k_pages, np.float64), np.asarray(v_pages, np.float64)
@@ -282,12 +284,13 @@ def paged_decode_ref(q, k_pages, v_pages, block_table, seq_lens, scale: float):
     O = np.zeros((B, H, vp.shape[3]))
     L = np.full((B, H), -np.inf)
     for b in range(B):
-        toks = [t for t in range(int(sl[b])) if 0 <= bt[b, t // P] < n_pages]
+        n = min(max(int(sl[b]), 0), bt.shape[1] * P)
+        toks = [t for t in range(n) if 0 <= bt[b, t // P] < n_pages]
         if not toks:
             continue
-        kb = np.stack([kp[bt[b, t // P], :, t % P, :] for t in toks], axis=1)  # [H, n, d]
+        kb = np.stack([kp[bt[b, t // P], :, t % P, :] for t in toks], axis=1)  # [H_kv, n, d]
         vb = np.stack([vp[bt[b, t // P], :, t % P, :] for t in toks], axis=1)
-        o, lse = decode_ref(q[b][None], kb[None], vb[None], scale)
+        o, lse = gqa_decode_ref(q[b][None], kb[None], vb[None], scale)
         O[b], L[b] = o[0], lse[0]
     return O, L
 
