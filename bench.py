@@ -123,8 +123,42 @@ def time_events(fn, stream, steps: int, warmup: int):
     return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
 
 
-def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int):
-    """Workloads beyond the graded step (timed after it, not part of ms_per_step)."""
+def to_pages_dev(x, table, page_size: int):
+    """Device-side layout change (input plumbing, untimed): contiguous cache x [B, H_kv, N, d] -> page pool
+    [B * N / page_size, H_kv, page_size, d] with logical block j of sequence b at page table[b, j]."""
+    import torch
+    B, Hkv, N, d = x.shape
+    nb = N // page_size
+    blocks = x.view(B, Hkv, nb, page_size, d).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, page_size, d)
+    pool = torch.empty_like(blocks)
+    pool[table.reshape(-1).long()] = blocks
+    return pool
+
+
+def time_paged(fa, syn, dev, stream, q, k, v, H: int, scale: float, S: int, steps: int, warmup: int, label: str):
+    """fa_decode_paged over k, v [B, H_kv, N, d] moved into 16-token pages under a shuffled block table."""
+    import torch
+    B, Hkv, N, d = k.shape
+    P = 16
+    nb = N // P
+    table = torch.from_numpy(syn.page_table(B, nb, B * nb, 8)).to(dev)
+    kp, vp = to_pages_dev(k, table, P), to_pages_dev(v, table, P)
+    sl = torch.full((B,), N, dtype=torch.int32, device=dev)
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_decode_paged_workspace_bytes(B, H, Hkv, N, d, S), dtype=torch.uint8, device=dev)
+    t = time_events(lambda: fa.fa_decode_paged(q, kp, vp, table, sl, o, lse, scale, S, ws, stream), stream, steps,
+                    warmup)
+    by = 2 * B * Hkv * N * d * 2 + 2 * B * H * d * 2 + table.numel() * 4 + B * 4  # K, V, q, o, table, lengths
+    return {"workload": f"fa_decode_paged bf16 B{B} H{H} H_kv{Hkv} N_kv{N} d{d}, {P}-token pages under a "
+                        f"shuffled block table, {S} splits + combine ({label})",
+            "value": round(by / (t * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "frac_of_peak": round(by / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "avg_ms": round(t, 4)}
+
+
+def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int, decode_inputs=None):
+    """Workloads beyond the graded step (timed after it, not part of ms_per_step).  decode_inputs: the
+    decode workload's (q, k, v, scale, splits) already on the device, reused for paged decode."""
     import torch
     out = {}
     w = syn.NEXT_WORKLOADS["chunk"]
@@ -157,7 +191,16 @@ def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int):
     out["gqa_decode"] = {"workload": f"fa_decode_gqa bf16 B{B} H{H} H_kv{Hkv} N_kv{N} d{d}, {S} splits + combine",
                          "value": round(by / (t * 1e-3) / 1e9, 1), "unit": "GB/s",
                          "frac_of_peak": round(by / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "avg_ms": round(t, 4)}
+    log("[bench] next: paged GQA decode")
+    out["paged_gqa_decode"] = time_paged(fa, syn, dev, stream, q, k, v, H, wq.scale, S, steps, warmup,
+                                         "same data as gqa_decode")
     del q, k, v, o, lse, ws
+    if decode_inputs is not None:
+        log("[bench] next: paged decode")
+        dq, dk, dv, dscale, dS = decode_inputs
+        out["paged_decode"] = time_paged(fa, syn, dev, stream, dq, dk, dv, dq.shape[1], dscale, dS, steps, warmup,
+                                         "same data as the decode step")
+        torch.cuda.empty_cache()
     # backward of the causal prefill workload (B1 H32 N8192 d128): dQ, dK, dV from O, LSE and dO
     w = syn.WORKLOADS["c3"]
     log(f"[bench] next: backward of {w.name}")
@@ -376,7 +419,8 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
     }
     if args.only in ("all", "next"):
-        rec["next"] = time_next(fa, syn, upload, dev, stream, args.steps, args.warmup)
+        rec["next"] = time_next(fa, syn, upload, dev, stream, args.steps, args.warmup,
+                                (dq, dk, dv, wd.scale, S) if run_d else None)
     if not args.no_cpu_baseline and args.only == "all":
         log("[bench] timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline()

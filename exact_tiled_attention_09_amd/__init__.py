@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_gqa_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.fa_decode_gqa_workspace_bytes.restype = sz
     L.fa_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp, i]
+    L.fa_decode_paged_num_splits.argtypes = [i, i, i, i, i]
+    L.fa_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.fa_decode_paged_workspace_bytes.restype = sz
+    L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp, i]
     L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
     L.fa_bwd_workspace_bytes.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp, i]
@@ -227,6 +231,38 @@ def fa_decode_gqa(q, k, v, o, lse, scale: float, num_splits: int, workspace, str
     _check(st, "fa_decode_gqa")
 
 
+def fa_decode_paged_num_splits(B: int, H_kv: int, max_seq_len: int, d: int, num_splits: int = 0) -> int:
+    return lib().fa_decode_paged_num_splits(B, H_kv, max_seq_len, d, num_splits)
+
+
+def fa_decode_paged_workspace_bytes(B: int, H: int, H_kv: int, max_seq_len: int, d: int, num_splits: int = 0) -> int:
+    return lib().fa_decode_paged_workspace_bytes(B, H, H_kv, max_seq_len, d, num_splits)
+
+
+def fa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, o, lse, scale: float, num_splits: int, workspace,
+                    stream=None):
+    """libfa fa_decode_paged: q [B,H,d]; k_pages/v_pages [num_pages,H_kv,page_size,d] (bf16); block_table
+    [B,max_blocks] and seq_lens [B] int32 device tensors; o [B,H,d]; lse [B,H] fp32 or None; workspace of at
+    least fa_decode_paged_workspace_bytes(B, H, H_kv, max_blocks * page_size, d, num_splits)."""
+    import torch
+    B, H, d = q.shape
+    n_pages, Hkv, P = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    max_blocks = block_table.shape[1] if block_table.dim() == 2 else -1
+    _check_tensor("q", q, (B, H, d), k_pages.dtype)
+    _check_tensor("k_pages", k_pages, (n_pages, Hkv, P, d), k_pages.dtype)
+    _check_tensor("v_pages", v_pages, (n_pages, Hkv, P, d), k_pages.dtype)
+    _check_tensor("block_table", block_table, (B, max_blocks), torch.int32)
+    _check_tensor("seq_lens", seq_lens, (B,), torch.int32)
+    _check_tensor("o", o, (B, H, d), k_pages.dtype)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H), torch.float32)
+    st = lib().fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(o),
+                               _ptr(lse), B, H, Hkv, n_pages, P, max_blocks, d, float(scale), int(num_splits),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
+                               _dtype_code(k_pages))
+    _check(st, "fa_decode_paged")
+
+
 def fa_bwd_workspace_bytes(B: int, H: int, N_q: int) -> int:
     return lib().fa_bwd_workspace_bytes(B, H, N_q)
 
@@ -318,4 +354,21 @@ def decode_gqa(q, k, v, scale: float | None = None, num_splits: int = 0, stream=
         raise FaError(FA_ERR_INVALID_ARG, "fa_decode_gqa_workspace_bytes", last_error())
     ws = torch.empty(n, dtype=torch.uint8, device=q.device)
     fa_decode_gqa(q, k, v, o, lse, scale, num_splits, ws, stream)
+    return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | None = None, num_splits: int = 0,
+                 stream=None):
+    """Allocate o, lse and the workspace and run fa_decode_paged; returns (o, lse)."""
+    import torch
+    B, H, d = q.shape
+    Hkv, P = k_pages.shape[1], k_pages.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    n = fa_decode_paged_workspace_bytes(B, H, Hkv, block_table.shape[-1] * P, d, num_splits)
+    if n == 0:
+        raise FaError(FA_ERR_INVALID_ARG, "fa_decode_paged_workspace_bytes", last_error())
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    fa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, o, lse, scale, num_splits, ws, stream)
     return o, lse

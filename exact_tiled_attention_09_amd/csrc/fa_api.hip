@@ -315,6 +315,101 @@ fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, fl
                       dtype);
 }
 
+int fa_decode_paged_num_splits(int B, int H_kv, int max_seq_len, int d, int num_splits) {
+  if (max_seq_len < 1) return 0;
+  return fa_decode_num_splits(B, H_kv, max_seq_len, d, num_splits);
+}
+
+size_t fa_decode_paged_workspace_bytes(int B, int H, int H_kv, int max_seq_len, int d, int num_splits) {
+  if (H_kv < 1 || H < H_kv || H % H_kv != 0) return 0;
+  const int S = fa_decode_paged_num_splits(B, H_kv, max_seq_len, d, num_splits);
+  if (S < 1) return 0;
+  int64_t n;
+  if (!mul_ok(n, {B, H, S, d + 1, 4}) || n > kMaxElems) return 0;
+  return (size_t)n;
+}
+
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
+                          const int* seq_lens, void* o, float* lse, int B, int H, int H_kv, int num_pages,
+                          int page_size, int max_blocks, int d, float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream, fa_dtype dtype) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o)
+    return fail(FA_ERR_INVALID_ARG, "q, k_pages, v_pages, block_table, seq_lens and o must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, k_pages, v_pages and o must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+    return fail(FA_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
+  if (B < 1 || H < 1 || H_kv < 1 || num_pages < 1 || max_blocks < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H, H_kv, num_pages and max_blocks must be >= 1");
+  if (H % H_kv != 0) return fail(FA_ERR_INVALID_ARG, "H must be a multiple of H_kv (got H=%d, H_kv=%d)", H, H_kv);
+  if (page_size < 1 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+    return fail(FA_ERR_INVALID_ARG, "page_size must be a power of two in [1, 2^20] (got %d)", page_size);
+  // Grouped heads on pages of >= 8 tokens go through the matrix-core split kernel (any group size); one
+  // query head per key/value head, or smaller pages, through the vector kernel (groups of 1, 2, 4, 8).
+  const int G = H / H_kv;
+  const bool mfma_path = G >= 2 && page_size >= 8;
+  if (!mfma_path && G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(FA_ERR_UNSUPPORTED, "paged decode with page_size < 8 is built for H / H_kv in {1, 2, 4, 8} (got %d)",
+                G);
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head size d=%d is not built (supported: 64, 128)", d);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  int64_t max_len, pool_el, q_el, tab_el;
+  // 2^30 keeps every token index of the kernel, range ends and chunk steps included, inside int
+  if (!mul_ok(max_len, {max_blocks, page_size}) || max_len > (1 << 30))
+    return fail(FA_ERR_INVALID_ARG, "max_blocks * page_size must be <= 2^30 (got %d * %d)", max_blocks, page_size);
+  if (!mul_ok(pool_el, {num_pages, H_kv, page_size, d}) || pool_el > kMaxElems || !mul_ok(q_el, {B, H, d}) ||
+      !mul_ok(tab_el, {B, max_blocks}) || tab_el > kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
+  if (num_splits < 0 || num_splits > max_len)
+    return fail(FA_ERR_INVALID_ARG, "num_splits must be in [0, max_blocks * page_size] (got %d)", num_splits);
+  const int S = fa_decode_paged_num_splits(B, H_kv, (int)max_len, d, num_splits);
+  int64_t grid;
+  if (S < 1 || !mul_ok(grid, {B, H_kv, S}) || grid > INT_MAX ||
+      (mfma_path && fa::prefill_bf16_grid(B, H_kv, G, d, S) > INT_MAX))
+    return fail(FA_ERR_INVALID_ARG, "launch grid too large");
+  const Range rq = span(q, q_el * 2), rk = span(k_pages, pool_el * 2), rv = span(v_pages, pool_el * 2);
+  const Range rt = span(block_table, tab_el * 4), rs = span(seq_lens, (size_t)B * 4);
+  const Range ro = span(o, q_el * 2);
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rt) || overlap(ro, rs))
+    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  const Range rl = span(lse, lse ? (size_t)B * H * 4 : 0);
+  if (lse && (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, rt) || overlap(rl, rs) ||
+              overlap(rl, ro)))
+    return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
+  if (dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "paged decode is built for bf16 only");
+  const size_t need = ws_bytes(B, H, d, S);
+  fa_status st = check_workspace(workspace, workspace_bytes, need);
+  if (st != FA_OK) return st;
+  const Range rw = span(workspace, need);
+  if (overlap(rw, rq) || overlap(rw, rk) || overlap(rw, rv) || overlap(rw, rt) || overlap(rw, rs) ||
+      overlap(rw, ro) || (lse && overlap(rw, rl)))
+    return fail(FA_ERR_INVALID_ARG, "workspace overlaps another tensor");
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = ws_o + (size_t)B * H * S * d;
+  if (mfma_path) {
+    // the G query heads of a key/value head are the query rows of one split forward over its pages
+    fa::PrefillArgs a{q, k_pages, v_pages, nullptr, nullptr, B, H_kv, G, (int)max_len, d, scale, false};
+    a.splits = S;
+    a.ws_o = ws_o;
+    a.ws_lse = ws_lse;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.num_pages = num_pages;
+    a.page_size = page_size;
+    a.max_blocks = max_blocks;
+    st = device_status(fa::launch_prefill_paged_bf16(a, (hipStream_t)stream), "fa_decode_paged split launch");
+  } else {
+    fa::PagedDecodeArgs a{q, k_pages, v_pages, block_table, seq_lens, B, H, H_kv, num_pages, page_size, max_blocks,
+                          d, scale, S, ws_o, ws_lse};
+    st = device_status(fa::launch_decode_paged_bf16(a, (hipStream_t)stream), "fa_decode_paged split launch");
+  }
+  if (st != FA_OK) return st;
+  fa::CombineArgs cmb{ws_o, ws_lse, o, lse, B, H, d, S};
+  return device_status(fa::launch_decode_combine_bf16(cmb, (hipStream_t)stream), "fa_decode_paged combine launch");
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N_q) {
   int64_t n;
   if (B < 1 || H < 1 || N_q < 1 || !mul_ok(n, {B, H, N_q, 4}) || n > kMaxElems) return 0;

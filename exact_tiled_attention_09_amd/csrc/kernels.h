@@ -20,6 +20,11 @@ struct PrefillArgs {
   int splits = 0;
   float* ws_o = nullptr;    // [B*H*N_q, splits, d]
   float* ws_lse = nullptr;  // [B*H*N_q, splits]
+  // paged key/value cache (launch_prefill_paged_bf16 only): H counts key/value heads, k and v are page pools
+  // [num_pages, H, page_size, d], N_kv is unused (lengths come from seq_lens on the device)
+  const int* block_table = nullptr;  // [B, max_blocks]
+  const int* seq_lens = nullptr;     // [B]
+  int num_pages = 0, page_size = 0, max_blocks = 0;
 };
 
 struct DecodeArgs {
@@ -31,6 +36,19 @@ struct DecodeArgs {
   int splits;
   float* ws_o;    // [B,H,S,d]
   float* ws_lse;  // [B,H,S]
+};
+
+struct PagedDecodeArgs {
+  const void* q;        // [B, H, d]
+  const void* k_pages;  // [num_pages, H_kv, page_size, d]
+  const void* v_pages;
+  const int* block_table;  // [B, max_blocks]
+  const int* seq_lens;     // [B]
+  int B, H, Hkv, num_pages, page_size, max_blocks, d;
+  float scale;
+  int splits;
+  float* ws_o;    // [B*H, S, d]
+  float* ws_lse;  // [B*H, S]
 };
 
 struct CombineArgs {
@@ -60,8 +78,12 @@ struct BwdArgs {
 // Each launcher assumes validated arguments and returns the launch status.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+// Split mode over a paged cache, no mask: writes the split partials of N_q query rows per key/value head.
+// Needs page_size >= 8 (a 1 KB load block never straddles a page).
+hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_split_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_combine_bf16(const CombineArgs& a, hipStream_t s);
+hipError_t launch_decode_paged_bf16(const PagedDecodeArgs& a, hipStream_t s);  // G = H / H_kv in {1, 2, 4, 8}
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 
 // Grid-size helpers shared with argument validation.

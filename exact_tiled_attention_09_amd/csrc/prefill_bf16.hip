@@ -55,6 +55,12 @@ struct PrefillParams {
   int S, split_tiles;
   float* __restrict__ ws_o;    // [B*H*N_q, S, D] fp32, O_s normalised
   float* __restrict__ ws_lse;  // [B*H*N_q, S] fp32, natural log; -inf for a row with no key in the range
+  // paged key/value cache (split mode, no mask): k, v are page pools [num_pages, H, 2^lg_page, D] (H here
+  // counts key/value heads), token t of sequence b is row t % 2^lg_page of page table[b][t >> lg_page], and
+  // the sequence has min(max(seq_lens[b], 0), max_blocks << lg_page) tokens.
+  const int* __restrict__ table;
+  const int* __restrict__ seq_lens;
+  int Hkv, num_pages, max_blocks, lg_page;
 };
 
 #ifndef FA_NW
@@ -99,8 +105,9 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
   return acc;
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED = false>
 __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(PrefillParams p) {
+  static_assert(!PAGED || (SPLIT && !CAUSAL), "the paged cache is read by the unmasked split mode only");
   using C = Cfg<D>;
   // One LDS array per stage and operand: the compiler can then tell that the direct loads into one
   // stage do not alias the fragment reads of the other, and does not wait for those loads before them.
@@ -121,7 +128,15 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const size_t head_q = (size_t)bh * p.Nq * D;
-  const size_t head_kv = (size_t)bh * p.Nkv * D;
+  int nkv = p.Nkv;  // keys of this (batch, head)
+  size_t head_kv = (size_t)bh * p.Nkv * D;
+  const int* __restrict__ tab = nullptr;
+  if constexpr (PAGED) {  // bh = b * H_kv + h_kv; the head's rows start at h_kv << lg_page inside every page
+    const int b = bh / p.Hkv;
+    nkv = min(max(p.seq_lens[b], 0), p.max_blocks << p.lg_page);
+    head_kv = (size_t)(bh - b * p.Hkv) * ((size_t)D << p.lg_page);
+    tab = p.table + (size_t)b * p.max_blocks;
+  }
   const uint16_t* __restrict__ qg = p.q + head_q;
   const uint16_t* __restrict__ kg = p.k + head_kv;
   const uint16_t* __restrict__ vg = p.v + head_kv;
@@ -139,16 +154,18 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
     qf[ks] = __builtin_bit_cast(bf16x8, x);
   }
 
-  int kv_end = p.Nkv;
-  if (CAUSAL) kv_end = min(p.Nkv, q0 + C::BR + p.off);
+  int kv_end = nkv;
+  if (CAUSAL) kv_end = min(nkv, q0 + C::BR + p.off);
   int t_beg = 0, n_tiles = (kv_end + C::BC - 1) / C::BC;  // tiles [t_beg, n_tiles) of this work-group
   if (SPLIT) {
-    t_beg = min(split * p.split_tiles, n_tiles);
-    n_tiles = min(t_beg + p.split_tiles, n_tiles);
+    // a paged sequence's own length is cut into S ranges (lengths are only known on the device)
+    const int per = PAGED ? (n_tiles + p.S - 1) / p.S : p.split_tiles;
+    t_beg = min(split * per, n_tiles);
+    n_tiles = min(t_beg + per, n_tiles);
   }
   // keys this wave needs (0 when the wave's rows lie past N_q)
-  const int wave_kv_end = qw0 >= p.Nq ? 0 : (CAUSAL ? min(p.Nkv, qw0 + 32 + p.off) : p.Nkv);
-  const int lim = CAUSAL ? min(p.Nkv - 1, qi + p.off) : p.Nkv - 1;  // last key this row may attend
+  const int wave_kv_end = qw0 >= p.Nq ? 0 : (CAUSAL ? min(nkv, qw0 + 32 + p.off) : nkv);
+  const int lim = CAUSAL ? min(nkv - 1, qi + p.off) : nkv - 1;  // last key this row may attend
 
   f32x16 oacc[C::MBD];
 #pragma unroll
@@ -167,16 +184,70 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
     ld_k[i] = r * C::ROWB + 16 * (pc ^ swz_k<D>(r));
     ld_v[i] = r * C::ROWB + 16 * (pc ^ swz_v<D>(r));
   }
+  // Paged cache: a 1 KB block (RPL rows, RPL <= 8 <= page size, blocks aligned to RPL) never straddles a
+  // page, so each block gets a descriptor of its own at its page row, spanning the block's rows that lie
+  // before the sequence end, or nothing (zeros land in LDS) when the table entry lies outside the pool.
+  // A tile's 64 keys span at most 64 / page size (<= 8) pages: lane i of every wave loads the tile's i-th
+  // entry (-1 if outside the pool), one tile ahead of the K / V loads that need it, and the blocks read
+  // their entry back with readlane.  absent0/1 hold, per stage, one bit per key of the tile whose entry
+  // lies outside the pool; those keys take the masked path and get zero weight, like keys past the end.
+  uint64_t absent0 = 0, absent1 = 0;
+  int ent_nx = -1;
+  auto fetch_entries = [&](int t) {
+    if constexpr (PAGED) {
+      const int kv0 = t * C::BC, lg = p.lg_page;
+      const int pg0 = kv0 >> lg, n_ent = ((min(kv0 + C::BC, nkv) - 1) >> lg) - pg0 + 1;
+      int e = -1;
+      if (lane < n_ent) e = tab[pg0 + lane];
+      ent_nx = (e >= 0 && e < p.num_pages) ? e : -1;
+    }
+  };
   auto load_tile = [&](int t, int stage) {
     const int kv0 = t * C::BC;
-    const int bytes = (p.Nkv - kv0) * C::ROWB;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
+    if constexpr (PAGED) {
+      const int lg = p.lg_page, pmask = (1 << lg) - 1;
+      const int ent = ent_nx;
+      const int n_ent = ((min(kv0 + C::BC, nkv) - 1) >> lg) - (kv0 >> lg) + 1;
+      const uint64_t holes = __builtin_amdgcn_ballot_w64(lane < n_ent && ent < 0);
+      uint64_t bad = 0;
+      if (holes) {
+        if (lg >= 6) {
+          bad = ~0ull;
+        } else {
+          const uint64_t page_keys = (1ull << (1 << lg)) - 1;
+          for (int i = 0; i < n_ent; ++i)
+            if ((holes >> i) & 1) bad |= page_keys << (i << lg);
+        }
+      }
+      if (stage == 0)
+        absent0 = bad;
+      else
+        absent1 = bad;
 #pragma unroll
-    for (int i = 0; i < C::LPT; ++i) {
-      const int blk = 1024 * (w * C::LPT + i);
-      load_lds16(rk, ld_k[i], kbuf(stage) + blk);
-      load_lds16(rv, ld_v[i], vbuf(stage) + blk);
+      for (int i = 0; i < C::LPT; ++i) {
+        const int rb = C::RPL * (w * C::LPT + i);  // first row of the block within the tile
+        const int r0 = kv0 + rb;
+        const int e = __builtin_amdgcn_readlane(ent, lg >= 6 ? 0 : rb >> lg);
+        int bytes = 0;
+        size_t row_el = 0;
+        if (r0 < nkv && e >= 0) {
+          bytes = min(C::RPL, nkv - r0) * C::ROWB;
+          row_el = ((((size_t)e * p.Hkv) << lg) + (r0 & pmask)) * D;
+        }
+        const int blk = 1024 * (w * C::LPT + i);
+        load_lds16(make_rsrc(kg + row_el, bytes), ld_k[i] - rb * C::ROWB, kbuf(stage) + blk);
+        load_lds16(make_rsrc(vg + row_el, bytes), ld_v[i] - rb * C::ROWB, vbuf(stage) + blk);
+      }
+    } else {
+      const int bytes = (nkv - kv0) * C::ROWB;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
+#pragma unroll
+      for (int i = 0; i < C::LPT; ++i) {
+        const int blk = 1024 * (w * C::LPT + i);
+        load_lds16(rk, ld_k[i], kbuf(stage) + blk);
+        load_lds16(rv, ld_v[i], vbuf(stage) + blk);
+      }
     }
   };
 
@@ -224,11 +295,14 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
     // mask (diagonal and ragged-tail tiles only; the rest of the tile is one code path)
     if (masked) {
       const int rel = lim - kv0 - 4 * h;  // key offset within the tile allowed iff 8*(r/4) + (r%4) + 32*mb <= rel
+      const uint64_t ab = PAGED ? ((STAGE == 0 ? absent0 : absent1) >> (4 * h)) : 0;
 #pragma unroll
       for (int mb = 0; mb < C::NBLK; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * mb + 8 * (r >> 2) + (r & 3) > rel) S[mb][r] = kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 32 * mb + 8 * (r >> 2) + (r & 3);
+          if (kk > rel || (PAGED && ((ab >> kk) & 1))) S[mb][r] = kNegInf;
+        }
     }
     // Online softmax against the running reference maximum m: the weights are 2^(x - m).  Only the
     // first tile of a wave (m = -inf) and tiles whose weights would exceed 2^64 reduce the tile's
@@ -305,18 +379,23 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const bool more = t + 1 < n_tiles;
+    if (PAGED && more) fetch_entries(t + 1);
     auto next = [&]() {
       if (more) load_tile(t + 1, STAGE ^ 1);
     };
     const int kv0 = t * C::BC;
+    const bool holes = PAGED && (STAGE == 0 ? absent0 : absent1) != 0;
     if (kv0 < wave_kv_end)
-      compute_tile(stage_tag, (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off), kv0, next);
+      compute_tile(stage_tag, (kv0 + C::BC > nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off) || holes, kv0, next);
     else if (more)
       load_tile(t + 1, STAGE ^ 1);
   };
 
   // the two stages alternate from the first tile of the range, so stage = (t - t_beg) & 1
-  if (t_beg < n_tiles) load_tile(t_beg, 0);
+  if (t_beg < n_tiles) {
+    fetch_entries(t_beg);
+    load_tile(t_beg, 0);
+  }
   for (int t = t_beg; t < n_tiles; t += 2) {
     tile(std::integral_constant<int, 0>{}, t);
     if (t + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, t + 1);
@@ -367,7 +446,7 @@ int64_t prefill_bf16_grid(int B, int H, int Nq, int d, int splits) {
   return (int64_t)B * H * ((Nq + br - 1) / br) * (splits > 0 ? splits : 1);
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED = false>
 static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   using C = Cfg<D>;
   PrefillParams p;
@@ -387,13 +466,25 @@ static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   p.qxor = a.scale < 0.f ? 0x80008000u : 0u;
   p.ws_o = a.ws_o;
   p.ws_lse = a.ws_lse;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, SPLIT>), dim3(p.total), dim3(C::NT), 0, s, p);
+  p.table = a.block_table;
+  p.seq_lens = a.seq_lens;
+  p.Hkv = a.H;
+  p.num_pages = a.num_pages;
+  p.max_blocks = a.max_blocks;
+  int lg = 0;
+  while ((1 << lg) < a.page_size) ++lg;
+  p.lg_page = lg;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, SPLIT, PAGED>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
 int prefill_split_tiles(int Nkv, int S) {
   const int tiles = (Nkv + Cfg<128>::BC - 1) / Cfg<128>::BC;
   return (tiles + S - 1) / S;
+}
+
+hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, hipStream_t s) {
+  return a.d == 128 ? launch_d<128, false, true, true>(a, s) : launch_d<64, false, true, true>(a, s);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {

@@ -162,6 +162,47 @@ fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, fl
                         void* stream, fa_dtype dtype);
 
 /*
+ * fa_decode_paged -- decode against a paged KV cache (the paging scheme of the
+ * post "Paged Attention: Fixing the KV Cache Memory Problem", listed among the
+ * related posts of "Flash Attention Explained: Speed From Memory Movement": the
+ * cache is cut into fixed-size pages so that no sequence reserves memory for its
+ * maximum length, and a table maps each sequence's logical blocks to pages).
+ *
+ *   q            [B, H, d] bf16, one query per sequence and head.
+ *   k_pages,
+ *   v_pages      [num_pages, H_kv, page_size, d] bf16: the shared page pool.
+ *   block_table  [B, max_blocks] int32 (device): token t of sequence b is row
+ *                t % page_size of page block_table[b][t / page_size].  An entry
+ *                outside [0, num_pages) marks its tokens absent: they are not
+ *                read and take no part in the softmax (use -1 for padding).
+ *   seq_lens     [B] int32 (device): tokens of sequence b, used as
+ *                min(max(seq_lens[b], 0), max_blocks * page_size).
+ *   o            [B, H, d] bf16; lse [B, H] float32 or NULL.  A sequence with no
+ *                present token gets o = 0 and lse = -inf.
+ *
+ * Query head h reads key/value head h / (H / H_kv), H a multiple of H_kv.  With
+ * H / H_kv >= 2 and page_size >= 8 the group's query heads are the query rows of a
+ * matrix-core split forward over the pages (any group size); otherwise a vector
+ * kernel serves the group, which must then be 1, 2, 4 or 8 heads (else
+ * FA_ERR_UNSUPPORTED).  page_size is a power of two in [1, 2^20] and
+ * max_blocks * page_size <= 2^30.  No mask (every present token is seen).
+ * Lengths and the table are read on the device, so the host needs only the bound
+ * max_seq_len = max_blocks * page_size to size the work: num_splits in
+ * [0, max_blocks * page_size] (0 = auto, as fa_decode_num_splits for B*H_kv
+ * sequences of that length); each sequence's own length is cut into that many
+ * ranges.  workspace: >= fa_decode_paged_workspace_bytes(B, H, H_kv,
+ * max_blocks * page_size, d, num_splits) bytes, 16-byte aligned, overlapping no
+ * other argument.  Table entries and lengths are trusted only as far as the
+ * clamping above: any int32 value is memory-safe.  bf16 only.
+ */
+int fa_decode_paged_num_splits(int B, int H_kv, int max_seq_len, int d, int num_splits);
+size_t fa_decode_paged_workspace_bytes(int B, int H, int H_kv, int max_seq_len, int d, int num_splits);
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
+                          const int* seq_lens, void* o, float* lse, int B, int H, int H_kv, int num_pages,
+                          int page_size, int max_blocks, int d, float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream, fa_dtype dtype);
+
+/*
  * fa_bwd -- gradients of fa_fwd: given the forward's inputs, its output o and
  * log-sum-exp lse, and the upstream gradient dout = dL/dO, writes
  * dq = dL/dQ, dk = dL/dK, dv = dL/dV.

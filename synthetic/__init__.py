@@ -182,3 +182,32 @@ def custom(B, H, Nq, Nkv, d, dtype="bf16", causal=False, scale=None, seed=0, dis
     return Workload(f"custom_B{B}_H{H}_Nq{Nq}_Nkv{Nkv}_d{d}_{dtype}", B, H, Nq, Nkv, d, dtype, causal,
                     (1 / math.sqrt(d)) if scale is None else float(scale), seed,
                     dist or {"q": "normal", "k": "normal", "v": "normal"}, kind, num_splits)
+
+
+# ----------------------------------------------------------------------------- paged KV cache layout
+
+def page_table(B: int, n_blocks: int, num_pages: int, seed: int) -> np.ndarray:
+    """Block table int32 [B, n_blocks]: logical block j of sequence b gets physical page perm[b * n_blocks + j],
+    where perm is a seeded permutation of range(num_pages) (num_pages >= B * n_blocks)."""
+    if num_pages < B * n_blocks:
+        raise ValueError("the pool needs at least B * n_blocks pages")
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 100])))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    return perm[: B * n_blocks].reshape(B, n_blocks).copy()
+
+
+def paginate(x: np.ndarray, table: np.ndarray, num_pages: int, page_size: int, seed: int) -> np.ndarray:
+    """Scatter a contiguous cache x [B, H_kv, n_blocks * page_size, d] into a page pool
+    [num_pages, H_kv, page_size, d] as ``table`` says (token t of sequence b -> page table[b, t // page_size],
+    row t % page_size).  Pool pages that no entry names hold N(0,1)*8 filler from their own seeded stream, in
+    x's storage type, so that reading a wrong page shows."""
+    B, Hkv, N, d = x.shape
+    nb = N // page_size
+    if nb * page_size != N or table.shape != (B, nb):
+        raise ValueError("x must hold n_blocks whole pages per sequence, matching the table")
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 101])))
+    fill = rng.standard_normal((num_pages, Hkv, page_size, d), dtype=np.float32) * np.float32(8.0)
+    pool = fill if x.dtype == np.float32 else bf16_bits(fill)
+    blocks = x.reshape(B, Hkv, nb, page_size, d).transpose(0, 2, 1, 3, 4)  # [B, nb, Hkv, P, d]
+    pool[table.reshape(-1)] = blocks.reshape(B * nb, Hkv, page_size, d)
+    return pool

@@ -158,3 +158,46 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(x, x, x, torch.empty_like(x), None, 0.1, False)
+
+
+def paged(L, q=P(0), kp=P(1), vp=P(2), bt=P(3), sl=P(4), o=P(5), lse=P(6), B=2, H=4, Hkv=2, pages=4, psz=16,
+          mb=2, d=128, scale=0.1, S=2, ws=P(8), wsb=None, dtype=0):
+    if wsb is None:
+        wsb = fa.fa_decode_paged_workspace_bytes(2, 4, 2, 32, 128, 2)
+    return L.fa_decode_paged(q, kp, vp, bt, sl, o, lse, B, H, Hkv, pages, psz, mb, d, scale, S, ws, wsb, None, dtype)
+
+
+def test_paged_workspace_arithmetic(L):
+    assert fa.fa_decode_paged_workspace_bytes(2, 4, 2, 32, 128, 2) == 2 * 4 * 2 * 129 * 4
+    assert fa.fa_decode_paged_workspace_bytes(2, 4, 3, 32, 128, 2) == 0   # H not a multiple of H_kv
+    assert fa.fa_decode_paged_workspace_bytes(2, 4, 2, 0, 128, 2) == 0    # no length bound
+    assert fa.fa_decode_paged_num_splits(64, 8, 8192, 128, 0) == fa.fa_decode_num_splits(64, 8, 8192, 128, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), fa.FA_ERR_INVALID_ARG),
+    (dict(sl=None), fa.FA_ERR_INVALID_ARG),
+    (dict(sl=ctypes.c_void_p(5 * A + 2)), fa.FA_ERR_INVALID_ARG),      # seq_lens misaligned
+    (dict(kp=ctypes.c_void_p(2 * A + 8)), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),                             # H % H_kv != 0
+    (dict(H=12, Hkv=4, psz=4, mb=8), fa.FA_ERR_UNSUPPORTED),          # 3 per kv head on 4-token pages
+    (dict(H=32, Hkv=2, psz=2, mb=16), fa.FA_ERR_UNSUPPORTED),         # 16 per kv head on 2-token pages
+    (dict(psz=12), fa.FA_ERR_INVALID_ARG),                            # not a power of two
+    (dict(psz=0), fa.FA_ERR_INVALID_ARG),
+    (dict(psz=1 << 21), fa.FA_ERR_INVALID_ARG),
+    (dict(mb=1 << 27), fa.FA_ERR_INVALID_ARG),                        # max length past 2^30
+    (dict(pages=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(S=33), fa.FA_ERR_INVALID_ARG),                              # more splits than max_blocks * page_size
+    (dict(S=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=1), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(wsb=64), fa.FA_ERR_WORKSPACE),
+    (dict(o=P(3)), fa.FA_ERR_INVALID_ARG),                            # o overlaps the block table
+    (dict(lse=P(1)), fa.FA_ERR_INVALID_ARG),                          # lse inside the key pool
+    (dict(ws=P(4)), fa.FA_ERR_INVALID_ARG),                           # workspace overlaps seq_lens
+])
+def test_paged_rejects(L, kw, status):
+    assert paged(L, **kw) == status
+    assert fa.last_error() != ""

@@ -1,0 +1,194 @@
+"""GPU parity of decode against a paged KV cache (fa_decode_paged) with the fp64 oracle.
+
+Every case scatters a seeded contiguous cache into a shuffled page pool (unnamed pool pages hold large
+filler, so reading a wrong page shows) and compares O (<= 1.6e-2) and LSE (<= 1e-3) with paged_decode_ref.
+Sequences with no present token must give O = 0 and LSE = -inf exactly.  Groups of two or more query heads
+on pages of at least 8 tokens run on the matrix-core split kernel, everything else on the vector kernel;
+the cases cover both (the last column of CASES names the path).
+"""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from oracle import paged_decode_ref
+from tests.gpu_util import TOL_LSE, TOL_O, max_err, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+def fa():
+    import exact_tiled_attention_09_amd as m
+    return m
+
+
+def make_case(B, H, Hkv, d, P, n_blocks, extra_pages, seed, scale=None):
+    """Host arrays: q bits [B,H,d], pools [num_pages,Hkv,P,d] bits, table [B,n_blocks] int32, and f64 values."""
+    wq = syn.custom(B, H, 1, 1, d, "bf16", False, scale, seed=seed)
+    wkv = syn.custom(B, Hkv, 1, n_blocks * P, d, "bf16", False, scale, seed=seed + 1000)
+    hq = syn.make_tensor(wq, "q")[:, :, 0]
+    num_pages = B * n_blocks + extra_pages
+    table = syn.page_table(B, n_blocks, num_pages, seed)
+    kp = syn.paginate(syn.make_tensor(wkv, "k"), table, num_pages, P, seed)
+    vp = syn.paginate(syn.make_tensor(wkv, "v"), table, num_pages, P, seed + 1)
+    return wq.scale, hq, kp, vp, table
+
+
+def run(scale, hq, kp, vp, table, seq_lens, splits):
+    import torch
+    q, k, v = to_dev(hq, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16")
+    bt = torch.from_numpy(np.ascontiguousarray(table, np.int32)).cuda()
+    sl = torch.from_numpy(np.asarray(seq_lens, np.int32)).cuda()
+    o, lse = fa().decode_paged(q, k, v, bt, sl, scale, splits)
+    return to_host64(o), to_host64(lse)
+
+
+def check(O, L, hq, kp, vp, table, seq_lens, scale, what):
+    Oref, Lref = paged_decode_ref(syn.as_f64(hq, "bf16"), syn.as_f64(kp, "bf16"), syn.as_f64(vp, "bf16"), table,
+                                  seq_lens, scale)
+    empty = np.isneginf(Lref)
+    assert np.all(np.isneginf(L[empty])) and np.all(O[empty] == 0), "empty sequences must give O = 0, LSE = -inf"
+    eo, el = max_err(O[~empty], Oref[~empty]), max_err(L[~empty], Lref[~empty])
+    print(f"  {what}: max|dO|={eo:.3e} max|dLSE|={el:.3e} empty rows={int(empty.sum())}", flush=True)
+    assert eo <= TOL_O["bf16"], f"O error {eo}"
+    assert el <= TOL_LSE, f"LSE error {el}"
+
+
+def path(H, Hkv, P):
+    return "mfma" if H // Hkv >= 2 and P >= 8 else "vector"
+
+
+CASES = [
+    # B, H, H_kv, d, page_size, n_blocks, extra_pages, seq_lens, splits, scale
+    (4, 8, 8, 128, 16, 188, 5, (1, 100, 1000, 3000), 0, None),        # ragged, auto splits
+    (3, 16, 4, 64, 32, 40, 0, (1280, 777, 33), 3, None),               # 4 query heads per kv head
+    (2, 16, 2, 128, 1, 600, 9, (600, 513), 5, None),                   # one token per page, 8 per kv head
+    (2, 4, 2, 128, 2048, 2, 1, (4096, 2049), 4, None),                 # pages longer than a chunk
+    (2, 8, 1, 64, 64, 9, 3, (576, 65), 2, -0.3),                       # multi-query, negative scale
+    (1, 2, 2, 128, 16, 64, 0, (1024,), 16, 0.0),                       # uniform weights
+    (5, 4, 4, 64, 8, 8, 2, (64, 0, 7, 8, 9), 3, None),                 # an empty sequence, page edges
+    (1, 32, 8, 128, 16, 512, 0, (8192,), 16, None),                    # one long sequence
+    (3, 4, 2, 128, 4, 100, 7, (400, 1, 333), 3, None),                 # 2 per kv head on 4-token pages
+    (2, 8, 2, 64, 2, 300, 0, (600, 77), 0, None),                      # 4 per kv head on 2-token pages
+    (2, 12, 2, 64, 8, 40, 4, (320, 129), 4, None),                     # 6 per kv head; 8-token pages (d=64)
+    (2, 80, 2, 128, 32, 20, 0, (640, 300), 3, None),                   # 40 per kv head: two waves of rows
+    (1, 130, 1, 128, 64, 8, 1, (500,), 2, None),                       # 130 query heads: two query tiles
+    (2, 16, 1, 128, 16, 4, 0, (64, 63), 8, None),                      # more splits than key tiles
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}Hkv{}d{}P{}nb{}x{}_{}S{}s{}_".format(
+    *c[:7], "-".join(map(str, c[7])), *c[8:]) + path(c[1], c[2], c[4]))
+def test_paged_decode(case):
+    B, H, Hkv, d, P, nb, extra, seq_lens, S, scale = case
+    scale, hq, kp, vp, table = make_case(B, H, Hkv, d, P, nb, extra, 600 + CASES.index(case), scale)
+    print(f"[fa_decode_paged] {case}", flush=True)
+    O, L = run(scale, hq, kp, vp, table, seq_lens, S)
+    check(O, L, hq, kp, vp, table, seq_lens, scale, f"paged {case}")
+
+
+@pytest.mark.parametrize("H,Hkv,P", [(4, 2, 16), (4, 4, 16), (4, 2, 4), (16, 2, 64)],
+                         ids=lambda x: str(x))
+def test_absent_pages_and_clamped_lengths(H, Hkv, P):
+    """Table entries -1 and >= num_pages drop their tokens (one split range entirely absent); a length
+    beyond the table width is cut at it; a negative length is an empty sequence.  Both kernels."""
+    B, d = 4, 128
+    nb = 256 // P
+    scale, hq, kp, vp, table = make_case(B, H, Hkv, d, P, nb, 0, 650)
+    table = table.copy()
+    table[0, 0:nb // 2] = -1            # first half of sequence 0 absent: with 2 splits, range 0 is empty
+    table[1, 3 * nb // 16] = kp.shape[0]  # one page past the pool
+    table[1, 7 * nb // 16] = np.iinfo(np.int32).max
+    table[1, nb - 1] = -7               # the last page, inside a partial tile of the length below
+    table[2, :] = -1                    # every page absent
+    seq_lens = (256, 250, 256, 100000)  # sequence 3 is cut at 256 tokens
+    print(f"[fa_decode_paged] absent pages, clamped lengths H={H} H_kv={Hkv} P={P} ({path(H, Hkv, P)})",
+          flush=True)
+    O, L = run(scale, hq, kp, vp, table, seq_lens, 2)
+    check(O, L, hq, kp, vp, table, seq_lens, scale, "absent/clamped")
+    O2, L2 = run(scale, hq, kp, vp, table, (256, 250, 256, -5), 2)
+    check(O2, L2, hq, kp, vp, table, (256, 250, 256, -5), scale, "negative length")
+
+
+def test_in_order_pages_match_contiguous_decode():
+    """With pages laid out in order, paged decode equals fa_decode on the contiguous cache (same split
+    ranges, same chunking), and both sit within the oracle tolerance."""
+    import torch
+    B, H, d, P, N, S = 4, 8, 128, 16, 2048, 4
+    wq = syn.custom(B, H, 1, N, d, "bf16", False, None, seed=660)
+    hq = syn.make_tensor(wq, "q")[:, :, 0]
+    hk, hv = syn.make_tensor(wq, "k"), syn.make_tensor(wq, "v")
+    nb = N // P
+    table = np.arange(B * nb, dtype=np.int32).reshape(B, nb)
+    kp, vp = syn.paginate(hk, table, B * nb, P, 660), syn.paginate(hv, table, B * nb, P, 661)
+    print("[fa_decode_paged] in-order pages vs fa_decode", flush=True)
+    O, L = run(wq.scale, hq, kp, vp, table, (N,) * B, S)
+    o2, l2 = fa().decode(to_dev(hq, "bf16"), to_dev(hk, "bf16"), to_dev(hv, "bf16"), wq.scale, S)
+    assert max_err(O, to_host64(o2)) <= 1e-2 and max_err(L, to_host64(l2)) <= 1e-5
+    check(O, L, hq, kp, vp, table, (N,) * B, wq.scale, "in-order")
+    torch.cuda.synchronize()
+
+
+def test_in_order_pages_match_contiguous_gqa_decode():
+    """Grouped heads (matrix-core path): in-order pages against fa_decode_gqa on the contiguous cache."""
+    B, H, Hkv, d, P, N, S = 4, 16, 4, 128, 16, 2048, 4
+    wq = syn.custom(B, H, 1, 1, d, "bf16", False, None, seed=665)
+    wkv = syn.custom(B, Hkv, 1, N, d, "bf16", False, None, seed=666)
+    hq = syn.make_tensor(wq, "q")[:, :, 0]
+    hk, hv = syn.make_tensor(wkv, "k"), syn.make_tensor(wkv, "v")
+    nb = N // P
+    table = np.arange(B * nb, dtype=np.int32).reshape(B, nb)
+    kp, vp = syn.paginate(hk, table, B * nb, P, 665), syn.paginate(hv, table, B * nb, P, 666)
+    print("[fa_decode_paged] in-order pages vs fa_decode_gqa", flush=True)
+    O, L = run(wq.scale, hq, kp, vp, table, (N,) * B, S)
+    o2, l2 = fa().decode_gqa(to_dev(hq, "bf16"), to_dev(hk, "bf16"), to_dev(hv, "bf16"), wq.scale, S)
+    assert max_err(O, to_host64(o2)) <= 1e-2 and max_err(L, to_host64(l2)) <= 1e-5
+    check(O, L, hq, kp, vp, table, (N,) * B, wq.scale, "in-order grouped")
+
+
+@pytest.mark.parametrize("Hkv,P", [(2, 16), (8, 16), (2, 4)])
+def test_deterministic(Hkv, P):
+    scale, hq, kp, vp, table = make_case(2, 8, Hkv, 128, P, 1024 // P, 3, 670)
+    print(f"[fa_decode_paged] determinism H_kv={Hkv} P={P}", flush=True)
+    a = run(scale, hq, kp, vp, table, (1000, 777), 0)
+    b = run(scale, hq, kp, vp, table, (1000, 777), 0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_full_size_shuffled_pages_sampled():
+    """The decode workload's shape (B=64, H=32, 8192 keys, d=128) in 16-token pages under a shuffled table,
+    with ragged lengths; sampled sequences against the oracle run on their contiguous tokens (one token per
+    page, identity table), so the kernel's page lookups are checked against the unpaged data."""
+    import torch
+    w = syn.WORKLOADS["c5"]
+    B, H, N, d, P = w.B, w.H, w.Nkv, w.d, 16
+    nb = N // P
+    table = syn.page_table(B, nb, B * nb, 680)
+    rng = np.random.default_rng(680)
+    seq_lens = rng.integers(1, N + 1, size=B).astype(np.int32)
+    seq_lens[0], seq_lens[1] = N, 1
+    print("[fa_decode_paged] full-size shuffled pages: generating", flush=True)
+    hq = syn.make_tensor(w, "q")[:, :, 0]
+    hk, hv = syn.make_tensor(w, "k"), syn.make_tensor(w, "v")
+    bt = torch.from_numpy(table).cuda()
+    idx = bt.reshape(-1).long()
+
+    def to_pool(x):  # [B, H, N, d] -> [B * nb, H, P, d] with block (b, j) at page table[b, j]
+        blocks = to_dev(x, "bf16").view(B, H, nb, P, d).permute(0, 2, 1, 3, 4).reshape(B * nb, H, P, d)
+        pool = torch.empty_like(blocks)
+        pool[idx] = blocks
+        return pool
+
+    kp, vp = to_pool(hk), to_pool(hv)
+    q = to_dev(hq, "bf16")
+    sl = torch.from_numpy(seq_lens).cuda()
+    print("[fa_decode_paged] full-size shuffled pages: running", flush=True)
+    o, lse = fa().decode_paged(q, kp, vp, bt, sl, w.scale, 16)
+    O, L = to_host64(o), to_host64(lse)
+    for b in (0, 1, 17, 63):
+        n = int(seq_lens[b])
+        as_pages = lambda x: syn.as_f64(x[b, :, :n], "bf16").transpose(1, 0, 2)[:, :, None, :]  # [n, H, 1, d]
+        Oref, Lref = paged_decode_ref(syn.as_f64(hq[b:b + 1], "bf16"), as_pages(hk), as_pages(hv),
+                                      np.arange(n, dtype=np.int32)[None], (n,), w.scale)
+        eo, el = max_err(O[b], Oref[0]), max_err(L[b], Lref[0])
+        print(f"  b={b} n={n}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+        assert eo <= TOL_O["bf16"] and el <= TOL_LSE
