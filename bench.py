@@ -258,8 +258,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "f32", "next"], default="all",
-                    help="launch only this part of the step (for profiler runs); the JSON line is still printed")
+    ap.add_argument("--only", choices=["all", "step", "prefill", "decode", "f32", "next"], default="all",
+                    help="launch only this part (for profiler runs): 'step' is the timed step without the extra "
+                         "workloads, 'next' only the extra workloads; the JSON line is still printed")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the step, run 5 device-to-device copies of this many bytes (calibrates "
                          "the profiler's HBM byte counters against a copy of known size) and exit")
@@ -299,9 +300,9 @@ def main():
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
 
     wp, wd, w1 = syn.WORKLOADS["c3"], syn.WORKLOADS["c5"], syn.WORKLOADS["c1"]
-    run_p = args.only in ("all", "prefill")
-    run_d = args.only in ("all", "decode")
-    run_f = args.only in ("all", "f32")
+    run_p = args.only in ("all", "step", "prefill")
+    run_d = args.only in ("all", "step", "decode")
+    run_f = args.only in ("all", "step", "f32")
     S = wd.num_splits
     log(f"[bench] generating inputs: {wp.name}, {wd.name}, {w1.name} (only={args.only})")
     if run_p:

@@ -25,6 +25,11 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, int voff, v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, 0, 0, 0);
 }
 
+// The same with the non-temporal cache policy, for data that is read exactly once.
+__device__ __forceinline__ void load_lds16_nt(__amdgpu_buffer_rsrc_t r, int voff, void* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, 0, 0, 2);
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
