@@ -60,7 +60,8 @@ def traffic_from_profiles(kernel: str):
 TRAFFIC_KERNELS = {
     # name in traffic.json: (run directory prefix, kernel-name substring, kernel sources)
     "prefill_bf16_c3": ("prefill", "prefill_bf16_kernel",
-                        ["exact_tiled_attention_09_amd/csrc/prefill_bf16.hip", "exact_tiled_attention_09_amd/csrc/common.h"]),
+                        ["exact_tiled_attention_09_amd/csrc/prefill_bf16.hip", "exact_tiled_attention_09_amd/csrc/common.h",
+                         "exact_tiled_attention_09_amd/csrc/lds_tiles.h"]),
     "decode_split_c5": ("decode", "decode_split_kernel",
                         ["exact_tiled_attention_09_amd/csrc/decode.hip", "exact_tiled_attention_09_amd/csrc/common.h"]),
 }
@@ -195,11 +196,17 @@ def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int, decode_inpu
     out["paged_gqa_decode"] = time_paged(fa, syn, dev, stream, q, k, v, H, wq.scale, S, steps, warmup,
                                          "same data as gqa_decode")
     del q, k, v, o, lse, ws
+    if decode_inputs is None:  # --only next: the decode workload's inputs are not on the device yet
+        wd = syn.WORKLOADS["c5"]
+        decode_inputs = (upload(syn.make_tensor(wd, "q")[:, :, 0].copy(), "bf16"),
+                         upload(syn.make_tensor(wd, "k"), "bf16"), upload(syn.make_tensor(wd, "v"), "bf16"),
+                         wd.scale, wd.num_splits)
     if decode_inputs is not None:
         log("[bench] next: paged decode")
         dq, dk, dv, dscale, dS = decode_inputs
         out["paged_decode"] = time_paged(fa, syn, dev, stream, dq, dk, dv, dq.shape[1], dscale, dS, steps, warmup,
                                          "same data as the decode step")
+        del dq, dk, dv, decode_inputs
         torch.cuda.empty_cache()
     # backward of the causal prefill workload (B1 H32 N8192 d128): dQ, dK, dV from O, LSE and dO
     w = syn.WORKLOADS["c3"]
