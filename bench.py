@@ -158,7 +158,7 @@ def time_paged(fa, syn, dev, stream, q, k, v, H: int, scale: float, S: int, step
 
 
 def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int, decode_inputs=None):
-    """Workloads beyond the graded step (timed after it, not part of ms_per_step).  decode_inputs: the
+    """Workloads beyond the timed step (timed after it, not part of ms_per_step).  decode_inputs: the
     decode workload's (q, k, v, scale, splits) already on the device, reused for paged decode."""
     import torch
     out = {}
@@ -279,8 +279,8 @@ def main():
         write_traffic(args.write_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build runs on a single "
-              f"MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the library drives one "
+              f"MI355X per process; sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

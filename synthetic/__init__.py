@@ -96,7 +96,7 @@ WORKLOADS = {
                    kind="decode", num_splits=16),
 }
 
-# Workloads beyond the five graded ones: a chunk of 1000 new queries (not a multiple of any tile height)
+# Workloads beyond the five listed configurations: a chunk of 1000 new queries (not a multiple of any tile height)
 # appended to an 8192-key cache, bottom-right causal ("prefill against a cache").
 NEXT_WORKLOADS = {
     "chunk": Workload("chunked_causal_bf16_B1_H32_Nq1000_Nkv8192_d128", 1, 32, 1000, 8192, 128, "bf16", True,
