@@ -192,3 +192,48 @@ def test_full_size_shuffled_pages_sampled():
         eo, el = max_err(O[b], Oref[0]), max_err(L[b], Lref[0])
         print(f"  b={b} n={n}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
         assert eo <= TOL_O["bf16"] and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (8, 8)], ids=["mfma", "vector"])
+def test_pool_beyond_4gib(H, Hkv):
+    """Pages far into a pool larger than 4 GiB (64-bit page addressing in both kernels); lse may be NULL."""
+    import torch
+    B, d, P, nb = 2, 128, 16, 24
+    page_bytes = Hkv * P * d * 2
+    num_pages = (9 << 29) // page_bytes + 5            # ~4.5 GiB per pool
+    wq = syn.custom(B, H, 1, 1, d, "bf16", False, None, seed=690)
+    wkv = syn.custom(B, Hkv, 1, nb * P, d, "bf16", False, None, seed=691)
+    hq = syn.make_tensor(wq, "q")[:, :, 0]
+    hk, hv = syn.make_tensor(wkv, "k"), syn.make_tensor(wkv, "v")
+    table = (num_pages - 1 - 3 * np.arange(B * nb, dtype=np.int64)).astype(np.int32).reshape(B, nb)
+    seq_lens = np.array([nb * P, nb * P - 5], np.int32)
+    print(f"[fa_decode_paged] pool of {num_pages} pages ({num_pages * page_bytes / 2**30:.2f} GiB), H={H} H_kv={Hkv}",
+          flush=True)
+    kp = torch.empty((num_pages, Hkv, P, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    idx = torch.from_numpy(table.reshape(-1).astype(np.int64)).cuda()
+    for pool, x in ((kp, hk), (vp, hv)):
+        blocks = to_dev(x, "bf16").view(B, Hkv, nb, P, d).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, P, d)
+        pool[idx] = blocks
+    q = to_dev(hq, "bf16")
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.from_numpy(seq_lens).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    n = fa().fa_decode_paged_workspace_bytes(B, H, Hkv, nb * P, d, 0)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    fa().fa_decode_paged(q, kp, vp, bt, sl, o, lse, wq.scale, 0, ws)
+    o2 = torch.empty_like(q)
+    fa().fa_decode_paged(q, kp, vp, bt, sl, o2, None, wq.scale, 0, ws)
+    O, L = to_host64(o), to_host64(lse)
+    assert np.array_equal(O, to_host64(o2)), "lse = NULL must not change o"
+    for b in range(B):
+        n_b = int(seq_lens[b])
+        as_pages = lambda x: syn.as_f64(x[b, :, :n_b], "bf16").transpose(1, 0, 2)[:, :, None, :]
+        Oref, Lref = paged_decode_ref(syn.as_f64(hq[b:b + 1], "bf16"), as_pages(hk), as_pages(hv),
+                                      np.arange(n_b, dtype=np.int32)[None], (n_b,), wq.scale)
+        eo, el = max_err(O[b], Oref[0]), max_err(L[b], Lref[0])
+        print(f"  b={b}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+        assert eo <= TOL_O["bf16"] and el <= TOL_LSE
+    del kp, vp
+    torch.cuda.empty_cache()
