@@ -256,7 +256,51 @@ def cpu_baseline(target_s: float = 12.0):
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads or cores,
             "kind": "oracle",
             "sample": f"causal bf16 prefill B1 H32 N8192 d128: {heads} of 32 heads, every row, "
-                      f"{flops / 1e9:.1f} GFLOP in fp64 in {t_total:.1f} s on {cores} host cores"}
+                      f"{flops / 1e9:.1f} GFLOP in fp64 in {t_total:.1f} s on {cores} host cores",
+            "per_config": cpu_baseline_other_configs()}
+
+
+def cpu_baseline_other_configs(budget_s: float = 1.5):
+    """The oracle's rate on bounded samples of the other four workloads: whole heads (c1, c2), evenly spaced
+    full causal rows of one head (c4), whole decode rows (c5)."""
+    import synthetic as syn
+    from oracle import attention_ref, decode_ref
+    out = {}
+    for cfg in ("c1", "c2"):
+        w = syn.WORKLOADS[cfg]
+        heads, flops, t_total = 0, 0, 0.0
+        pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+        per_head = w.flops // len(pairs)
+        for b, h in pairs:
+            q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=[(b, h)]), w.dtype)[None] for t in "qkv")
+            t0 = time.perf_counter()
+            attention_ref(q, k, v, w.scale, w.causal)
+            t_total += time.perf_counter() - t0
+            flops += per_head
+            heads += 1
+            if t_total >= budget_s:
+                break
+        out[cfg] = {"value": round(flops / t_total / 1e12, 4), "unit": "TFLOP/s", "wall_s": round(t_total, 3),
+                    "sample": f"{w.name}: {heads} of {len(pairs)} heads"}
+    w = syn.WORKLOADS["c4"]
+    q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=[(0, 0)]), "bf16")[None] for t in "qkv")
+    rows = np.linspace(0, w.Nq - 1, 512).astype(np.int64)
+    t0 = time.perf_counter()
+    attention_ref(q, k, v, w.scale, True, rows=rows)
+    t_total = time.perf_counter() - t0
+    flops = int(4 * w.d * (rows + 1).sum())
+    out["c4"] = {"value": round(flops / t_total / 1e12, 4), "unit": "TFLOP/s", "wall_s": round(t_total, 3),
+                 "sample": f"{w.name}: 512 evenly spaced causal rows of head 0"}
+    w = syn.WORKLOADS["c5"]
+    pairs = [(b, h) for b in range(0, w.B, 4) for h in range(0, w.H, 8)][:64]
+    q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=pairs), "bf16")[None] for t in "qkv")
+    t0 = time.perf_counter()
+    decode_ref(q[:, :, 0], k, v, w.scale)
+    t_total = time.perf_counter() - t0
+    by = len(pairs) * (2 * w.Nkv * w.d * 2 + w.d * 2)
+    out["c5"] = {"value": round(by / t_total / 1e9, 3), "unit": "GB/s (bf16 q, K, V bytes)",
+                 "wall_s": round(t_total, 3), "sample": f"{w.name}: {len(pairs)} of {w.B * w.H} (b, h) rows"}
+    return out
 
 
 def main():
@@ -403,6 +447,7 @@ def main():
             "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_profiles("prefill_bf16_c3"),
             "avg_kernel_ms": round(float(t_prefill.mean()), 4),
+            "median_kernel_ms": round(float(np.median(t_prefill)), 4),
             "min_kernel_ms": round(float(t_prefill.min()), 4),
         },
         "decode": {
@@ -419,6 +464,8 @@ def main():
                 "frac": round(split_gbs / PEAK_HBM_GBS, 4),
                 "traffic": traffic_from_profiles("decode_split_c5"),
                 "avg_kernel_ms": round(float(t_split.mean()), 4),
+                "median_kernel_ms": round(float(np.median(t_split)), 4),
+                "min_kernel_ms": round(float(t_split.min()), 4),
                 "combine_avg_kernel_ms": round(float(t_comb.mean()), 4),
             },
         },
