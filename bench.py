@@ -162,6 +162,22 @@ def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int, decode_inpu
     decode workload's (q, k, v, scale, splits) already on the device, reused for paged decode."""
     import torch
     out = {}
+    # the two other causal bf16 prefill workloads (fa_fwd), for reference next to the timed one
+    for cfg in ("c2", "c4"):
+        w = syn.WORKLOADS[cfg]
+        log(f"[bench] next: {w.name}")
+        q, k, v = (upload(syn.make_tensor(w, t), "bf16") for t in "qkv")
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        ts = []
+        for _ in range(3):  # medians of three event-timed batches
+            ts.append(time_events(lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream), stream, steps, warmup))
+        t = float(np.median(ts))
+        out[f"prefill_{cfg}"] = {"workload": f"fa_fwd {w.name}", "value": round(w.flops / (t * 1e-3) / 1e12, 2),
+                                 "unit": "TFLOP/s",
+                                 "frac_of_peak": round(w.flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                 "avg_ms": round(t, 4)}
+        del q, k, v, o, lse
     w = syn.NEXT_WORKLOADS["chunk"]
     log(f"[bench] next: {w.name}")
     q, k, v = (upload(syn.make_tensor(w, t), "bf16") for t in "qkv")
