@@ -27,9 +27,11 @@
 //  * K and V tiles of 64 keys go global -> LDS with direct 16-byte loads (buffer_load_dwordx4 ... lds,
 //    no staging registers), double-buffered with one barrier per tile: tile t+1 is in flight while
 //    tile t is computed.  The loads of tile t+1 are issued right after the S MFMAs of tile t, so they
-//    land during the softmax rather than during fragment reads.  16-byte chunks are XOR-swizzled within each row (the swizzle is applied through
-//    each lane's source address) so every fragment read hits distinct banks, and fragment addresses
-//    are per-lane bases plus compile-time offsets.
+//    land during the softmax rather than during fragment reads.  16-byte chunks are XOR-swizzled within
+//    each row (the swizzle is applied through each lane's source address) so every fragment read hits
+//    distinct banks, and fragment addresses are per-lane bases plus compile-time offsets.
+//  * Fragment reads run ahead of their MFMAs: K fragments four deep (scheduling groups), and all V^T
+//    fragments of a tile are read before its softmax, so their LDS latency passes under the vector work.
 //  * Causal tiles above the diagonal are never loaded; a wave skips the math of tiles that lie fully
 //    above its rows; only diagonal and ragged-tail tiles evaluate the mask.
 //  * Work-group ids are remapped so each XCD walks contiguous (head, tile) ranges, heaviest causal
@@ -73,6 +75,9 @@ struct PrefillParams {
 #define FA_OCC 2
 #endif
 constexpr float kBig = 0x1p64f;  // weights above this trigger a move of the reference maximum
+// instruction classes of __builtin_amdgcn_sched_group_barrier, and the K fragment read-ahead
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+constexpr int kKDepth = 4;
 
 template <int D>
 struct Cfg {
@@ -300,7 +305,31 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
         S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
       }
     }
+    // Keep kKDepth K fragment reads in flight ahead of the MFMAs (left alone, the compiler reads two
+    // ahead, and each MFMA pair waits for LDS latency): reads 0..kKDepth-1, then MFMA / read pairs.
+    {
+      constexpr int NK = C::KS * C::NBLK;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKDepth, 0);
+#pragma unroll
+      for (int i = 0; i < NK - kKDepth; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKDepth, 0);
+    }
     next();
+    // V^T fragments of the whole tile, read now so their LDS latency passes during the softmax
+    bf16x8 vfr[2 * C::NBLK][C::MBD];
+#pragma unroll
+    for (int kc = 0; kc < 2 * C::NBLK; ++kc)
+#pragma unroll
+      for (int mbd = 0; mbd < C::MBD; ++mbd) {
+        const uint8_t* vb = svb + v_off[mbd] + 16 * kc * C::ROWB;
+        const s16x4 lo = lds_read_tr16(vb);
+        const s16x4 hi = lds_read_tr16(vb + 8 * C::ROWB);
+        vfr[kc][mbd] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    __builtin_amdgcn_sched_barrier(0);
     // mask (diagonal and ragged-tail tiles only; the rest of the tile is one code path)
     if (masked) {
       const int rel = lim - kv0 - 4 * h;  // key offset within the tile allowed iff 8*(r/4) + (r%4) + 32*mb <= rel
@@ -370,13 +399,8 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
 #pragma unroll
     for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
 #pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd) {
-        const uint8_t* vb = svb + v_off[mbd] + 16 * kc * C::ROWB;
-        const s16x4 lo = lds_read_tr16(vb);
-        const s16x4 hi = lds_read_tr16(vb + 8 * C::ROWB);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[kc], oacc[mbd], 0, 0, 0);
-      }
+      for (int mbd = 0; mbd < C::MBD; ++mbd)
+        oacc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[kc][mbd], P[kc], oacc[mbd], 0, 0, 0);
     }
   };
 
