@@ -58,3 +58,22 @@ def test_workload_arithmetic():
         ws = syn.custom(1, 1, nq, nkv, 64, causal=True)
         brute = sum(1 for i in range(nq) for j in range(nkv) if j <= i + nkv - nq)
         assert ws.allowed_pairs == brute
+
+
+def test_page_table_and_paginate():
+    """The paged layout helpers: a seeded permutation of distinct pages, and a scatter that the gather
+    through the same table undoes exactly, with unnamed pages holding filler."""
+    t = syn.page_table(3, 5, 20, seed=7)
+    assert t.shape == (3, 5) and t.dtype == np.int32
+    assert len(set(t.reshape(-1).tolist())) == 15 and t.min() >= 0 and t.max() < 20
+    assert np.array_equal(t, syn.page_table(3, 5, 20, seed=7))
+    x = syn.bf16_bits(np.random.default_rng(1).standard_normal((3, 2, 5 * 4, 8)).astype(np.float32))
+    pool = syn.paginate(x, t, 20, 4, seed=7)
+    assert pool.shape == (20, 2, 4, 8) and pool.dtype == x.dtype
+    for b in range(3):
+        for tok in range(20):
+            assert np.array_equal(pool[t[b, tok // 4], :, tok % 4, :], x[b, :, tok, :])
+    unnamed = sorted(set(range(20)) - set(t.reshape(-1).tolist()))
+    assert len(unnamed) == 5 and all(np.any(pool[u] != 0) for u in unnamed)
+    with pytest.raises(ValueError):
+        syn.page_table(3, 5, 14, seed=7)  # a pool smaller than the blocks it must hold
