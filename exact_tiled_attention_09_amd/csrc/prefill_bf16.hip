@@ -36,6 +36,11 @@
 //    above its rows; only diagonal and ragged-tail tiles evaluate the mask.
 //  * Work-group ids are remapped so each XCD walks contiguous (head, tile) ranges, heaviest causal
 //    query tiles first.
+// Modes (template flags): SPLIT cuts each query tile's keys into S ranges of whole tiles, one
+// work-group each, and writes fp32 partials (O_s normalised, LSE_s) that the decode combine merges; it
+// serves short query chunks against a long cache and grouped-head decode (the G query heads of a
+// key/value head are its query rows).  PAGED (with SPLIT, no mask) reads K and V through a block table
+// from a page pool.  NT gives the K / V loads the non-temporal policy when one query tile reads them.
 #include <type_traits>
 
 #include "common.h"
