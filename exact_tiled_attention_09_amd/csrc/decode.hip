@@ -8,9 +8,9 @@
 //
 // Split kernel (512 threads): a key row of d bf16 is read by d/8 lanes with one 16-byte load each,
 // so a wave reads 64*16 contiguous-row bytes per load instruction.  K and V are read once, so the loads
-// are non-temporal (they do not displace reusable lines; +7% HBM throughput measured against plain loads).  The range is processed in
-// chunks of up to kChunk keys: (A) scores q.k with v_dot2_f32_bf16 and a reduction over the d/8
-// lanes of the row, kept in LDS; (B) chunk max and exponentials 2^(s*c - m) with a work-group
+// are non-temporal (they do not displace reusable lines; +7% HBM throughput measured against plain
+// loads).  The range is processed in chunks of up to kChunk keys: (A) scores q.k with v_dot2_f32_bf16
+// and a DPP reduction over the d/8 lanes of the row, kept in LDS; (B) chunk max and exponentials 2^(s*c - m) with a work-group
 // reduction, and the running (m, l) update; (C) the value sum, each lane accumulating 8 output
 // columns over its keys in fp32.  Chunks after the first rescale the running sums by 2^(m_old - m).
 // The per-group partial outputs are summed through LDS at the end.
