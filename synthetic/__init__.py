@@ -11,6 +11,9 @@ Recipe (one independent stream per tensor slice):
   * the slice is drawn as float32 in C order: ``standard_normal`` for N(0,1),
     ``2*random()-1`` for U(-1,1), and ``4*standard_normal`` for the scaled
     queries of the peaked-softmax workload (scaling by a power of two is exact);
+    stress inputs for the tests use ``16*standard_normal`` ("normal16"),
+    ``0.5 + 0.1*standard_normal`` ("pos") and ``0.02*j + 0.1*standard_normal``
+    for row j ("ramp": scores that rise along the keys);
   * bf16 workloads round the float32 draws to bfloat16 with
     round-to-nearest-even (bit manipulation, no library conversion).
 
@@ -113,6 +116,13 @@ def draw_f32(seed: int, tensor: str, b: int, h: int, n: int, d: int, dist: str) 
         return rng.standard_normal((n, d), dtype=np.float32) * np.float32(4.0)
     if dist == "uniform":
         return rng.random((n, d), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+    if dist == "normal16":  # very peaked rows
+        return rng.standard_normal((n, d), dtype=np.float32) * np.float32(16.0)
+    if dist == "pos":       # positive queries: 0.5 + 0.1 N(0,1)
+        return rng.standard_normal((n, d), dtype=np.float32) * np.float32(0.1) + np.float32(0.5)
+    if dist == "ramp":      # rows that grow along the sequence: 0.02 j + 0.1 N(0,1), so later keys score higher
+        ramp = (np.arange(n, dtype=np.float32) * np.float32(0.02))[:, None]
+        return rng.standard_normal((n, d), dtype=np.float32) * np.float32(0.1) + ramp
     raise ValueError(f"unknown distribution {dist!r}")
 
 

@@ -229,3 +229,45 @@ def test_decode_split_then_combine_equals_decode():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     assert torch.equal(ws, ws2)
+
+
+# ----------------------------------------------------------------------------- stress inputs
+
+STRESS = [
+    # B, H, Nq, Nkv, d, dtype, causal, q dist, k dist
+    (1, 2, 1000, 1000, 128, "bf16", True, "pos", "ramp"),     # scores rise along the keys: the reference
+    (1, 2, 1000, 1000, 128, "bf16", False, "pos", "ramp"),    # maximum must move every few tiles
+    (1, 2, 1000, 1000, 64, "bf16", True, "pos", "ramp"),
+    (1, 1, 700, 700, 128, "f32", True, "pos", "ramp"),
+    (1, 2, 500, 500, 128, "bf16", True, "normal16", "normal"),  # one key dominates almost every row
+    # fp32 keeps the 2e-5 bar only while the fp32 score sums are accurate to ~1e-6: at 16x queries their
+    # rounding alone reaches ~3e-5 in O, so the fp32 peaked case uses the 4x queries of the c2 workload
+    (1, 2, 500, 500, 64, "f32", False, "normal4", "normal"),
+]
+
+
+@pytest.mark.parametrize("case", STRESS, ids=lambda c: "B{}H{}q{}kv{}d{}{}{}_{}_{}".format(*c))
+def test_stress_inputs(case):
+    B, H, Nq, Nkv, d, dtype, causal, dq, dk = case
+    w = syn.custom(B, H, Nq, Nkv, d, dtype, causal, None, seed=300 + STRESS.index(case),
+                   dist={"q": dq, "k": dk, "v": "normal"})
+    host, f64 = inputs(w)
+    O, L = run_fwd(w, host)
+    Oref, Lref = attention_ref(f64["q"], f64["k"], f64["v"], w.scale, w.causal)
+    check(w, O, L, Oref, Lref)
+
+
+def test_stress_rising_scores_split_and_decode():
+    """Rising scores through the split-KV forward (several ranges) and through decode."""
+    w = syn.custom(1, 2, 300, 2000, 128, "bf16", True, None, seed=320, dist={"q": "pos", "k": "ramp", "v": "normal"})
+    host, f64 = inputs(w)
+    q, k, v = (to_dev(host[t], "bf16") for t in "qkv")
+    print("[fa_fwd_split] rising scores", flush=True)
+    o, lse = fa().attention_split(q, k, v, 5, w.scale, True)
+    Oref, Lref = attention_ref(f64["q"], f64["k"], f64["v"], w.scale, True)
+    check(w, to_host64(o), to_host64(lse), Oref, Lref, " split")
+    print("[fa_decode] rising scores", flush=True)
+    qd = q[:, :, -1].contiguous()
+    od, ld = fa().decode(qd, k, v, w.scale, 4)
+    Od, Ld = attention_ref(f64["q"][:, :, -1:], f64["k"], f64["v"], w.scale, False)
+    check(w, to_host64(od)[:, :, None], to_host64(ld)[:, :, None], Od, Ld, " decode")
