@@ -22,6 +22,9 @@ namespace fa {
 namespace {
 constexpr int kDecThreads = 512;
 constexpr int kChunk = 1024;
+// K rows loaded per lane before their scores are reduced (16: +6% on B64 H32 N_kv8192 d128, at four
+// waves per SIMD instead of eight)
+constexpr int kScoreBatch = 16;
 }  // namespace
 
 struct DecodeParams {
@@ -130,11 +133,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
   for (int cb = k0; cb < k1; cb += kChunk) {
     const int n = min(kChunk, k1 - cb);
     // (A) scores, in log2 units
-#pragma unroll 8
-    for (int j = grp; j < n; j += KPI) {
-      const u32x4 kv = load16_nt(kg + (size_t)(cb + j) * D);
-      const float part = row_sum<LPR>(dot8_bf16(qv, kv));
-      if (sl == 0) sc[j] = part * p.c;
+    for (int j0 = grp; j0 < n; j0 += kScoreBatch * KPI) {
+      // the batch's loads first: the row reductions are cross-lane operations, which keep the compiler
+      // from unrolling a loop with a run-time trip count, so the batching is written out
+      u32x4 kv[kScoreBatch];
+#pragma unroll
+      for (int u = 0; u < kScoreBatch; ++u) {
+        const int j = j0 + u * KPI;
+        kv[u] = j < n ? load16_nt(kg + (size_t)(cb + j) * D) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kScoreBatch; ++u) {
+        const int j = j0 + u * KPI;
+        const float part = row_sum<LPR>(dot8_bf16(qv, kv[u]));
+        if (sl == 0 && j < n) sc[j] = part * p.c;
+      }
     }
     __syncthreads();
     // (B) chunk max, exponentials, chunk sum
@@ -268,16 +281,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_paged_kernel(PagedParams p
     }
     __syncthreads();
     // (A) scores of the G query heads, in log2 units (-inf for absent tokens)
-#pragma unroll 4
-    for (int j = grp; j < n; j += KPI) {
-      const int t = cb + j;
-      const int pg = ptab[(t >> lg) - pg0];
-      u32x4 kv = {0u, 0u, 0u, 0u};
-      if (pg >= 0) kv = load16_nt(kg + (size_t)pg * page_elems + (size_t)(t & pmask) * D);
+    // K rows per lane in flight: 8 for one head (16, as in the contiguous kernel, measured 7% slower here
+    // with the page lookups), 4 for grouped heads (registers grow with G)
+    constexpr int NB = G == 1 ? 8 : 4;
+    for (int j0 = grp; j0 < n; j0 += NB * KPI) {
+      u32x4 kv[NB];
+      bool here[NB];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float part = row_sum<LPR>(dot8_bf16(qv[g], kv));
-        if (sl == 0) sc[g][j] = pg >= 0 ? part * p.c : kNegInf;
+      for (int u = 0; u < NB; ++u) {
+        const int j = j0 + u * KPI;
+        const int t = cb + j;
+        const int pg = j < n ? ptab[(t >> lg) - pg0] : -1;
+        here[u] = pg >= 0;
+        kv[u] = here[u] ? load16_nt(kg + (size_t)pg * page_elems + (size_t)(t & pmask) * D) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int j = j0 + u * KPI;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float part = row_sum<LPR>(dot8_bf16(qv[g], kv[u]));
+          if (sl == 0 && j < n) sc[g][j] = here[u] ? part * p.c : kNegInf;
+        }
       }
     }
     __syncthreads();
