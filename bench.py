@@ -194,7 +194,8 @@ def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int, decode_inpu
                               "fa_fwd_single_pass_tflops": round(w.flops / (t * 1e-3) / 1e12, 2)}
     del q, k, v, o, lse, ws
     # grouped key/value decode: 32 query heads over 8 key/value heads, 8192 cached keys
-    B, H, Hkv, N, d, S = 64, 32, 8, 8192, 128, 8
+    B, H, Hkv, N, d = 64, 32, 8, 8192, 128
+    S = fa.fa_decode_gqa_num_splits(B, H, Hkv, N, d, 0)  # the library's own choice (4 here)
     wq = syn.custom(B, H, 1, 1, d, "bf16", False, None, seed=6)
     wkv = syn.custom(B, Hkv, 1, N, d, "bf16", False, None, seed=7)
     log(f"[bench] next: GQA decode B{B} H{H} H_kv{Hkv} N_kv{N} d{d}")
