@@ -26,8 +26,8 @@
 //    one d per lane, in exactly that key order.
 //  * K and V tiles of 64 keys go global -> LDS with direct 16-byte loads (buffer_load_dwordx4 ... lds,
 //    no staging registers), double-buffered with one barrier per tile: tile t+1 is in flight while
-//    tile t is computed.  The loads of tile t+1 are issued right after the S MFMAs of tile t, so they
-//    land during the softmax rather than during fragment reads.  16-byte chunks are XOR-swizzled within
+//    tile t is computed.  The loads of tile t+1 are issued right after the S MFMAs of tile t (and the
+//    V^T fragment reads), so they land during the softmax rather than during fragment reads.  16-byte chunks are XOR-swizzled within
 //    each row (the swizzle is applied through each lane's source address) so every fragment read hits
 //    distinct banks, and fragment addresses are per-lane bases plus compile-time offsets.
 //  * Fragment reads run ahead of their MFMAs: K fragments four deep (scheduling groups), and all V^T
@@ -322,8 +322,8 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKDepth, 0);
     }
-    next();
-    // V^T fragments of the whole tile, read now so their LDS latency passes during the softmax
+    // V^T fragments of the whole tile, read now so their LDS latency passes during the softmax; the next
+    // tile's loads go out right after them (+0.7% over the other order)
     bf16x8 vfr[2 * C::NBLK][C::MBD];
 #pragma unroll
     for (int kc = 0; kc < 2 * C::NBLK; ++kc)
@@ -335,6 +335,7 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
         vfr[kc][mbd] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     __builtin_amdgcn_sched_barrier(0);
+    next();
     // mask (diagonal and ragged-tail tiles only; the rest of the tile is one code path)
     if (masked) {
       const int rel = lim - kv0 - 4 * h;  // key offset within the tile allowed iff 8*(r/4) + (r%4) + 32*mb <= rel
