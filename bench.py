@@ -157,6 +157,28 @@ def time_paged(fa, syn, dev, stream, q, k, v, H: int, scale: float, S: int, step
             "frac_of_peak": round(by / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "avg_ms": round(t, 4)}
 
 
+def time_backward(fa, syn, upload, dev, stream, w, steps: int, warmup: int):
+    """fa_bwd on a causal bf16 workload, the forward's O and LSE as input; TFLOP/s at 2.5x the forward's flops."""
+    import torch
+    log(f"[bench] next: backward of {w.name}")
+    q, k, v = (upload(syn.make_tensor(w, t), "bf16") for t in "qkv")
+    do = upload(syn.make_tensor(w, "do"), "bf16")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq), dtype=torch.uint8, device=dev)
+    reps = max(3, steps // 4) if w.Nq >= 8192 else steps
+    t = time_events(lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, w.scale, True, ws, stream), stream,
+                    reps, warmup)
+    fl = 2.5 * w.flops  # five products of 2*d flops per allowed pair (S, dP, dV, dQ, dK)
+    tf = fl / (t * 1e-3) / 1e12
+    return {"workload": f"fa_bwd causal bf16 B{w.B} H{w.H} N{w.Nq} d{w.d} (dQ, dK, dV)",
+            "value": round(tf, 2), "unit": "TFLOP/s", "flops_per_call": fl,
+            "flops_convention": "2.5x the forward's 4*d per allowed pair",
+            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "avg_ms": round(t, 4)}
+
+
 def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int, decode_inputs=None):
     """Workloads beyond the timed step (timed after it, not part of ms_per_step).  decode_inputs: the
     decode workload's (q, k, v, scale, splits) already on the device, reused for paged decode."""
@@ -225,24 +247,10 @@ def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int, decode_inpu
                                          "same data as the decode step")
         del dq, dk, dv, decode_inputs
         torch.cuda.empty_cache()
-    # backward of the causal prefill workload (B1 H32 N8192 d128): dQ, dK, dV from O, LSE and dO
-    w = syn.WORKLOADS["c3"]
-    log(f"[bench] next: backward of {w.name}")
-    q, k, v = (upload(syn.make_tensor(w, t), "bf16") for t in "qkv")
-    do = upload(syn.make_tensor(w, "do"), "bf16")
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
-    fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq), dtype=torch.uint8, device=dev)
-    t = time_events(lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, w.scale, True, ws, stream), stream,
-                    max(3, steps // 4), warmup)
-    fl = 2.5 * w.flops  # five products of 2*d flops per allowed pair (S, dP, dV, dQ, dK)
-    out["backward"] = {"workload": "fa_bwd causal bf16 B1 H32 N8192 d128 (dQ, dK, dV)",
-                       "value": round(fl / (t * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                       "flops_per_call": fl, "flops_convention": "2.5x the forward's 4*d per allowed pair",
-                       "frac_of_peak": round(fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                       "avg_ms": round(t, 4)}
+    # backward of the causal prefill workloads (B1 H32 N8192 d128; B4 H16 N2048 d64): dQ, dK, dV from O, LSE
+    # and dO
+    out["backward"] = time_backward(fa, syn, upload, dev, stream, syn.WORKLOADS["c3"], steps, warmup)
+    out["backward_d64"] = time_backward(fa, syn, upload, dev, stream, syn.WORKLOADS["c2"], steps, warmup)
     return out
 
 
@@ -427,21 +435,30 @@ def main():
     t_prefill, t_split, t_comb, t_f32 = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
     t_step = ms(0, 4)
 
-    rate = lambda work, ms_: work / (ms_ * 1e-3) if ms_ > 0 else 0.0  # noqa: E731
-    pf_tflops = rate(wp.flops, t_prefill.mean()) / 1e12
+    # parts left out by --only report null rather than a rate over an empty interval
+    def rate(work, ms_, ran, unit):
+        return round(work / (ms_ * 1e-3) / unit, 3) if ran and ms_ > 0 else None
+
+    def frac(x, peak):
+        return None if x is None else round(x / peak, 4)
+
+    def kms(t, ran, f=np.mean):
+        return round(float(f(t)), 4) if ran else None
+
+    pf_tflops = rate(wp.flops, t_prefill.mean(), run_p, 1e12)
     split_bytes = 2 * wd.B * wd.H * wd.Nkv * wd.d * 2 + wd.B * wd.H * wd.d * 2   # K, V, q read once
-    split_gbs = rate(split_bytes, t_split.mean()) / 1e9
-    dec_gbs = rate(wd.io_bytes, t_split.mean() + t_comb.mean()) / 1e9
-    f32_tflops = rate(w1.flops, t_f32.mean()) / 1e12
+    split_gbs = rate(split_bytes, t_split.mean(), run_d, 1e9)
+    dec_gbs = rate(wd.io_bytes, t_split.mean() + t_comb.mean(), run_d, 1e9)
+    f32_tflops = rate(w1.flops, t_f32.mean(), run_f, 1e12)
 
     rec = {
         "metric": "prefill TFLOP/s & % bf16 MFMA peak; decode KV-read GB/s & % HBM peak",
-        "value": round(pf_tflops, 2),
+        "value": pf_tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(float(t_step.mean()), 4),
+        "ms_per_step": kms(t_step, args.only in ("all", "step")),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -458,35 +475,35 @@ def main():
         "roofline": {
             "kernel": "prefill_bf16_kernel<128,...,causal>",
             "bound": "mfma",
-            "achieved": round(pf_tflops, 2),
+            "achieved": pf_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": frac(pf_tflops, PEAK_BF16_TFLOPS),
             "traffic": traffic_from_profiles("prefill_bf16_c3"),
-            "avg_kernel_ms": round(float(t_prefill.mean()), 4),
-            "median_kernel_ms": round(float(np.median(t_prefill)), 4),
-            "min_kernel_ms": round(float(t_prefill.min()), 4),
+            "avg_kernel_ms": kms(t_prefill, run_p),
+            "median_kernel_ms": kms(t_prefill, run_p, np.median),
+            "min_kernel_ms": kms(t_prefill, run_p, np.min),
         },
         "decode": {
-            "value": round(dec_gbs, 1),
+            "value": dec_gbs,
             "unit": "GB/s",
-            "frac_of_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
-            "ms": round(float(t_split.mean() + t_comb.mean()), 4),
+            "frac_of_peak": frac(dec_gbs, PEAK_HBM_GBS),
+            "ms": kms(t_split + t_comb, run_d),
             "roofline": {
                 "kernel": "decode_split_kernel<128>",
                 "bound": "hbm",
-                "achieved": round(split_gbs, 1),
+                "achieved": split_gbs,
                 "peak": PEAK_HBM_GBS,
                 "unit": "GB/s",
-                "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                "frac": frac(split_gbs, PEAK_HBM_GBS),
                 "traffic": traffic_from_profiles("decode_split_c5"),
-                "avg_kernel_ms": round(float(t_split.mean()), 4),
-                "median_kernel_ms": round(float(np.median(t_split)), 4),
-                "min_kernel_ms": round(float(t_split.min()), 4),
-                "combine_avg_kernel_ms": round(float(t_comb.mean()), 4),
+                "avg_kernel_ms": kms(t_split, run_d),
+                "median_kernel_ms": kms(t_split, run_d, np.median),
+                "min_kernel_ms": kms(t_split, run_d, np.min),
+                "combine_avg_kernel_ms": kms(t_comb, run_d),
             },
         },
-        "fp32_prefill": {"value": round(f32_tflops, 3), "unit": "TFLOP/s", "avg_kernel_ms": round(float(t_f32.mean()), 4)},
+        "fp32_prefill": {"value": f32_tflops, "unit": "TFLOP/s", "avg_kernel_ms": kms(t_f32, run_f)},
         "wall_s_timed": round(wall, 4),
         "gpu": torch.cuda.get_device_name(0),
     }

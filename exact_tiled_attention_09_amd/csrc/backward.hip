@@ -14,10 +14,11 @@
 //    with a lane pair per query).  It also computes D from dO and O and stores it for the next kernel.
 //    Per 64-key tile: S^T = K Q^T and dP^T = V dO^T (K, V fragments from LDS), dS^T in registers,
 //    dQ^T += K^T dS^T (K^T through ds_read_b64_tr_b16 of the same K tile).
-//  * bwd_dkdv_kernel (two passes, dV then dK): one work-group per (b, h, 128 keys), the same layout with
-//    the roles of queries and keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query tile
-//    streamed through LDS: S = Q K^T, then dV^T += dO^T P; or S, dP = dO V^T and dK^T += Q^T dS (dO^T,
-//    Q^T through transposing reads).
+//  * bwd_dkdv_kernel: one work-group per (b, h, 128 keys), the same layout with the roles of queries and
+//    keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query tile streamed through LDS:
+//    S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through transposing
+//    reads).  At d = 64 one pass forms both; at d = 128 both accumulators do not fit beside the rest at
+//    two waves per SIMD, so a dV pass and a dK pass run one after the other.
 // Tiles read both row-wise (ds_read_b128) and transposed (ds_read_b64_tr_b16) use a swizzle that keeps
 // both access patterns on distinct banks.
 #include "common.h"
@@ -258,16 +259,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------------------------------------- dK, dV
 
-// One kernel body for dV (WANT_DK = false: S, P, dV^T += dO^T P) and dK (WANT_DK = true: S, dP, dS,
-// dK^T += Q^T dS).  Computing them in two passes recomputes S once more but keeps each pass within the
-// register budget of two waves per SIMD (one fused pass needs both 32x128 accumulators, the K and V
-// fragments and both score tiles at once, and spills).
-template <int D, bool CAUSAL, bool WANT_DK>
+// Which gradients one bwd_dkdv_kernel launch forms.
+enum BwdKvMode : int {
+  kGradV = 0,   // S, P, dV^T += dO^T P
+  kGradK = 1,   // S, dP, dS, dK^T += Q^T dS
+  kGradKV = 2,  // both from one S and dP
+};
+
+// One kernel body for the three modes.  The fused mode saves recomputing S and re-streaming Q, dO
+// (32 MFMAs per 32x32 key-query block instead of 40) but holds both D x 32 accumulators: at d = 128
+// that needs more than the 256 registers of two waves per SIMD, and at one wave per SIMD it was slower
+// than the two passes, so d = 128 runs kGradV then kGradK.
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
+  constexpr bool WANT_DK = MODE != kGradV;  // dP, dS and the V rows are needed
+  constexpr bool BOTH = MODE == kGradKV;
+  static_assert(!BOTH || D == 64, "the fused mode fits the register budget at d = 64 only");
   __shared__ __attribute__((aligned(16))) uint8_t lq0[C::TQ], ldo0[C::TQ], lq1[C::TQ], ldo1[C::TQ];
   __shared__ __attribute__((aligned(16))) float ll0[C::BQ], ld0[C::BQ], ll1[C::BQ], ld1[C::BQ];
-  // V of the work-group's 128 keys (B operand of dP = dO V^T; dK pass only)
+  // V of the work-group's 128 keys (B operand of dP = dO V^T; not needed by the dV pass)
   __shared__ __attribute__((aligned(16))) uint8_t lvk[WANT_DK ? C::BR * C::ROWB : 16];
   auto qbuf = [&](int st) -> uint8_t* { return st == 0 ? lq0 : lq1; };
   auto obuf = [&](int st) -> uint8_t* { return st == 0 ? ldo0 : ldo1; };
@@ -311,9 +322,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   const int t0 = CAUSAL ? max(0, k0 - p.off) / C::BQ : 0;
   const int wave_q_first = kw0 >= p.Nkv ? p.Nq : (CAUSAL ? max(0, kw0 - p.off) : 0);
 
-  f32x16 acc[C::MBD];
+  f32x16 acc[C::MBD];                // dV^T (kGradV) or dK^T
+  f32x16 accv[BOTH ? C::MBD : 1];    // dV^T in the fused mode
 #pragma unroll
   for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
+#pragma unroll
+  for (int mbd = 0; mbd < (BOTH ? C::MBD : 1); ++mbd) accv[mbd] = f32x16{};
 
   int ld_off[C::LPT_Q];
 #pragma unroll
@@ -366,10 +380,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     next();
     const float* lt = lbuf(st);
     const float* dt = dbuf(st);
-    bf16x8 bf[2];  // P (dV pass) or dS (dK pass), packed for the B operand
+    bf16x8 bf[2];  // P (kGradV) or dS, packed for the B operand
+    bf16x8 bp[2];  // P in the fused mode
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      float x[8];
+      float x[8], xp[8];
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {
         const int g = 2 * kc + g2;
@@ -382,12 +397,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
           float pr = exp2_hw(fmaf(S[r], c, -l4[e] * kLog2e));
           if (masked && kj > qr0 + 8 * g + 4 * h + e + p.off) pr = 0.f;
           x[4 * g2 + e] = WANT_DK ? pr * (dP[r] - d4[e]) : pr;
+          xp[4 * g2 + e] = pr;
         }
       }
       u32x4 pk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
       bf[kc] = __builtin_bit_cast(bf16x8, pk);
+      if constexpr (BOTH) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(xp[2 * i], xp[2 * i + 1]);
+        bp[kc] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+    if constexpr (BOTH) {  // dV^T += dO^T P
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int mbd = 0; mbd < C::MBD; ++mbd)
+          accv[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ob + 16 * kc * C::ROWB, trq[mbd]), bp[kc],
+                                                              accv[mbd], 0, 0, 0);
     }
     // dV^T += dO^T P  or  dK^T += Q^T dS
     const uint8_t* ab = WANT_DK ? qb : ob;
@@ -423,6 +452,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   if (key_ok) {
     if (WANT_DK) store_rowT<D>(p.dk + head_kv + (size_t)kj * D, acc, p.scale, h);
     else store_rowT<D>(p.dv + head_kv + (size_t)kj * D, acc, 1.f, h);
+    if constexpr (BOTH) store_rowT<D>(p.dv + head_kv + (size_t)kj * D, accv, 1.f, h);
   }
 }
 
@@ -454,11 +484,16 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(p.total_q), dim3(C::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3(p.total_k), dim3(C::NT), 0, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3(p.total_k), dim3(C::NT), 0, s, p);
-  return hipGetLastError();
+  if constexpr (D == 64) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kGradKV>), dim3(p.total_k), dim3(C::NT), 0, s, p);
+    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kGradV>), dim3(p.total_k), dim3(C::NT), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kGradK>), dim3(p.total_k), dim3(C::NT), 0, s, p);
+    return hipGetLastError();
+  }
 }
 
 int64_t bwd_bf16_grid(int B, int H, int Nq, int Nkv) {
