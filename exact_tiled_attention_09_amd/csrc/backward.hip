@@ -267,9 +267,9 @@ enum BwdKvMode : int {
 };
 
 // One kernel body for the three modes.  The fused mode saves recomputing S and re-streaming Q, dO
-// (32 MFMAs per 32x32 key-query block instead of 40) but holds both D x 32 accumulators: at d = 128
-// that needs more than the 256 registers of two waves per SIMD, and at one wave per SIMD it was slower
-// than the two passes, so d = 128 runs kGradV then kGradK.
+// (D/4 MFMAs per 32x32 key-query block instead of 5 D/16) but holds both D x 32 accumulators: at
+// d = 128 that needs more than the 256 registers of two waves per SIMD, and at one wave per SIMD it was
+// slower than the two passes, so d = 128 runs kGradV then kGradK.
 template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
