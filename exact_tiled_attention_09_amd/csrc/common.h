@@ -38,6 +38,9 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __builtin_bi
 // The value held by the lane 32 positions away (lane l reads lane l ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// Compute units of the gfx950 parts this library targets (MI350X, MI355X: 8 XCDs x 32).
+constexpr int kNumCu = 256;
+
 // Work-group id remapped so that consecutive logical ids land on the same XCD.  The dispatcher hands
 // work-groups to the 8 XCDs round-robin; XCD x receives physical ids x, x+8, x+16, ...  This maps them
 // to the contiguous logical range of that XCD, so tiles that share K/V also share one L2.

@@ -68,6 +68,7 @@ struct PrefillParams {
   const int* __restrict__ table;
   const int* __restrict__ seq_lens;
   int Hkv, num_pages, max_blocks, lg_page;
+  int pair;  // causal, unsplit: work-group j runs query tile n_qt-1-j, then tile j (set by the launcher)
 };
 
 #ifndef FA_NW
@@ -135,346 +136,358 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
   auto vbuf = [&](int st) -> uint8_t* { return st == 0 ? lds_v0 : lds_v1; };
 
   const int lid = xcd_logical_id(blockIdx.x, p.total);
-  const int per_bh = SPLIT ? p.n_qt * p.S : p.n_qt;
+  // Paired causal tiles: query tile i sees about i + 1 key blocks, so tiles n_qt-1-j and j together cost
+  // the same for every j.  Without pairing the longest tiles set the end of a grid that spans a few
+  // rounds of resident work-groups; with it every work-group carries the same load.
+  const bool pair = CAUSAL && !SPLIT && p.pair;
+  const int per_bh = SPLIT ? p.n_qt * p.S : (pair ? (p.n_qt + 1) / 2 : p.n_qt);
   const int bh = lid / per_bh;
-  int qt = lid - bh * per_bh, split = 0;
+  int qt_lo = lid - bh * per_bh, split = 0;
   if (SPLIT) {
-    split = qt % p.S;
-    qt /= p.S;
+    split = qt_lo % p.S;
+    qt_lo /= p.S;
   }
-  if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles first
-  const int q0 = qt * C::BR;
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, h = lane >> 5;
-  const size_t head_q = (size_t)bh * p.Nq * D;
-  int nkv = p.Nkv;  // keys of this (batch, head)
-  size_t head_kv = (size_t)bh * p.Nkv * D;
-  const int* __restrict__ tab = nullptr;
-  if constexpr (PAGED) {  // bh = b * H_kv + h_kv; the head's rows start at h_kv << lg_page inside every page
-    const int b = bh / p.Hkv;
-    nkv = min(max(p.seq_lens[b], 0), p.max_blocks << p.lg_page);
-    head_kv = (size_t)(bh - b * p.Hkv) * ((size_t)D << p.lg_page);
-    tab = p.table + (size_t)b * p.max_blocks;
-  }
-  const uint16_t* __restrict__ qg = p.q + head_q;
-  const uint16_t* __restrict__ kg = p.k + head_kv;
-  const uint16_t* __restrict__ vg = p.v + head_kv;
-  const int qw0 = q0 + w * 32;  // first query row of this wave
-  const int qi = qw0 + l32;     // this lane's query row
-  const float c = p.c;
-
-  // Q^T fragments: lane holds query qi, d = ks*16 + 8h .. +7.
-  bf16x8 qf[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < p.Nq) x = load16(qg + (size_t)qi * D + ks * 16 + 8 * h);
-    x ^= p.qxor;
-    qf[ks] = __builtin_bit_cast(bf16x8, x);
-  }
-
-  int kv_end = nkv;
-  if (CAUSAL) kv_end = min(nkv, q0 + C::BR + p.off);
-  int t_beg = 0, n_tiles = (kv_end + C::BC - 1) / C::BC;  // tiles [t_beg, n_tiles) of this work-group
-  if (SPLIT) {
-    // a paged sequence's own length is cut into S ranges (lengths are only known on the device)
-    const int per = PAGED ? (n_tiles + p.S - 1) / p.S : p.split_tiles;
-    t_beg = min(split * per, n_tiles);
-    n_tiles = min(t_beg + per, n_tiles);
-  }
-  // keys this wave needs (0 when the wave's rows lie past N_q)
-  const int wave_kv_end = qw0 >= p.Nq ? 0 : (CAUSAL ? min(nkv, qw0 + 32 + p.off) : nkv);
-  const int lim = CAUSAL ? min(nkv - 1, qi + p.off) : nkv - 1;  // last key this row may attend
-
-  f32x16 oacc[C::MBD];
-#pragma unroll
-  for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[mbd] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f, lh_run = 0.f;
-
-  // ---------------------------------------------------------------- global -> LDS (direct, no registers)
-  // Load i of wave w fills the 1 KB block (w * LPT + i) of a tile: rows RPL*(w*LPT+i) + lane/CH, physical
-  // chunk lane%CH, which holds logical chunk (lane%CH) ^ swizzle(row).  The per-lane byte offsets within
-  // a tile are fixed; each tile gets a buffer resource starting at its first key and ending at N_kv, so
-  // the loads need no vector address arithmetic and rows past N_kv read zeros (their scores are masked).
-  int ld_k[C::LPT], ld_v[C::LPT];
-#pragma unroll
-  for (int i = 0; i < C::LPT; ++i) {
-    const int r = C::RPL * (w * C::LPT + i) + lane / C::CH, pc = lane % C::CH;
-    ld_k[i] = r * C::ROWB + 16 * (pc ^ swz_k<D>(r));
-    ld_v[i] = r * C::ROWB + 16 * (pc ^ swz_v<D>(r));
-  }
-  // Paged cache: a 1 KB block (RPL rows, RPL <= 8 <= page size, blocks aligned to RPL) never straddles a
-  // page, so each block gets a descriptor of its own at its page row, spanning the block's rows that lie
-  // before the sequence end, or nothing (zeros land in LDS) when the table entry lies outside the pool.
-  // A tile's 64 keys span at most 64 / page size (<= 8) pages: lane i of every wave loads the tile's i-th
-  // entry (-1 if outside the pool), one tile ahead of the K / V loads that need it, and the blocks read
-  // their entry back with readlane.  absent0/1 hold, per stage, one bit per key of the tile whose entry
-  // lies outside the pool; those keys take the masked path and get zero weight, like keys past the end.
-  uint64_t absent0 = 0, absent1 = 0;
-  int ent_nx = -1;
-  auto fetch_entries = [&](int t) {
-    if constexpr (PAGED) {
-      const int kv0 = t * C::BC, lg = p.lg_page;
-      const int pg0 = kv0 >> lg, n_ent = ((min(kv0 + C::BC, nkv) - 1) >> lg) - pg0 + 1;
-      int e = -1;
-      if (lane < n_ent) e = tab[pg0 + lane];
-      ent_nx = (e >= 0 && e < p.num_pages) ? e : -1;
+  const int qt_hi = CAUSAL ? p.n_qt - 1 - qt_lo : qt_lo;  // heaviest query tiles first
+  const int n_pass = (pair && qt_lo != qt_hi) ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int qt = pass == 0 ? qt_hi : qt_lo;
+    if (pass > 0) __syncthreads();  // every wave is done with the LDS stages before they are refilled
+    const int q0 = qt * C::BR;
+    // the lane-derived offsets below are recomputed per pass instead of being held (and spilled) across both
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const size_t head_q = (size_t)bh * p.Nq * D;
+    int nkv = p.Nkv;  // keys of this (batch, head)
+    size_t head_kv = (size_t)bh * p.Nkv * D;
+    const int* __restrict__ tab = nullptr;
+    if constexpr (PAGED) {  // bh = b * H_kv + h_kv; the head's rows start at h_kv << lg_page inside every page
+      const int b = bh / p.Hkv;
+      nkv = min(max(p.seq_lens[b], 0), p.max_blocks << p.lg_page);
+      head_kv = (size_t)(bh - b * p.Hkv) * ((size_t)D << p.lg_page);
+      tab = p.table + (size_t)b * p.max_blocks;
     }
-  };
-  auto load_tile = [&](int t, int stage) {
-    const int kv0 = t * C::BC;
-    if constexpr (PAGED) {
-      const int lg = p.lg_page, pmask = (1 << lg) - 1;
-      const int ent = ent_nx;
-      const int n_ent = ((min(kv0 + C::BC, nkv) - 1) >> lg) - (kv0 >> lg) + 1;
-      const uint64_t holes = __builtin_amdgcn_ballot_w64(lane < n_ent && ent < 0);
-      uint64_t bad = 0;
-      if (holes) {
-        if (lg >= 6) {
-          bad = ~0ull;
-        } else {
-          const uint64_t page_keys = (1ull << (1 << lg)) - 1;
-          for (int i = 0; i < n_ent; ++i)
-            if ((holes >> i) & 1) bad |= page_keys << (i << lg);
-        }
-      }
-      if (stage == 0)
-        absent0 = bad;
-      else
-        absent1 = bad;
-#pragma unroll
-      for (int i = 0; i < C::LPT; ++i) {
-        const int rb = C::RPL * (w * C::LPT + i);  // first row of the block within the tile
-        const int r0 = kv0 + rb;
-        const int e = __builtin_amdgcn_readlane(ent, lg >= 6 ? 0 : rb >> lg);
-        int bytes = 0;
-        size_t row_el = 0;
-        if (r0 < nkv && e >= 0) {
-          bytes = min(C::RPL, nkv - r0) * C::ROWB;
-          row_el = ((((size_t)e * p.Hkv) << lg) + (r0 & pmask)) * D;
-        }
-        const int blk = 1024 * (w * C::LPT + i);
-        load16_lds(make_rsrc(kg + row_el, bytes), ld_k[i] - rb * C::ROWB, kbuf(stage) + blk);
-        load16_lds(make_rsrc(vg + row_el, bytes), ld_v[i] - rb * C::ROWB, vbuf(stage) + blk);
-      }
-    } else {
-      const int bytes = (nkv - kv0) * C::ROWB;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
-#pragma unroll
-      for (int i = 0; i < C::LPT; ++i) {
-        const int blk = 1024 * (w * C::LPT + i);
-        load16_lds(rk, ld_k[i], kbuf(stage) + blk);
-        load16_lds(rv, ld_v[i], vbuf(stage) + blk);
-      }
-    }
-  };
+    const uint16_t* __restrict__ qg = p.q + head_q;
+    const uint16_t* __restrict__ kg = p.k + head_kv;
+    const uint16_t* __restrict__ vg = p.v + head_kv;
+    const int qw0 = q0 + w * 32;  // first query row of this wave
+    const int qi = qw0 + l32;     // this lane's query row
+    const float c = p.c;
 
-  // ---------------------------------------------------------------- fragment addresses (bytes)
-  // K (A operand of S^T): row 32*mb + l32, logical chunk 2ks + h.
-  int k_off[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_k<D>(l32));
-  // V^T (A operand of O^T) through ds_read_b64_tr_b16: in lane group G = lane/16 (h = G/2, dh = G%2),
-  // lane j points at row key0 + j/4, d = 32*mbd + 16*dh + 4*(j%4); lane i then receives
-  // V[key0 + t][32*mbd + 16*dh + i], t = 0..3, with key0 = 16*kc + 8*u + 4*h.  The swizzle of those
-  // rows only depends on j/4, so each mbd has one per-lane base and (kc, u) are immediate offsets.
-  const int tr_j = lane & 15, tr_dh = (lane >> 4) & 1, tr_row = 4 * h + tr_j / 4;
-  int v_off[C::MBD];
-#pragma unroll
-  for (int mbd = 0; mbd < C::MBD; ++mbd) {
-    const int d0 = 32 * mbd + 16 * tr_dh + 4 * (tr_j & 3);
-    v_off[mbd] = tr_row * C::ROWB + 16 * ((d0 >> 3) ^ swz_v<D>(tr_row)) + 2 * (d0 & 7);
-  }
-
-  // ---------------------------------------------------------------- one tile
-  // `next()` issues this wave's loads of the next tile.  It runs right after the S MFMAs are issued, so
-  // the data lands in LDS during the softmax, when the wave reads no fragments (direct LDS writes that
-  // land during the fragment reads of the MFMA phases slow those reads down).
-  auto compute_tile = [&](auto stage_tag, bool masked, int kv0, auto&& next) {
-    constexpr int STAGE = decltype(stage_tag)::value;
-    const uint8_t* sb = kbuf(STAGE);
-    const uint8_t* svb = vbuf(STAGE);
-    // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks).  The wave raises its issue
-    // priority for its MFMA phases and drops it for the softmax, so when both waves of a SIMD are
-    // ready the matrix-core work goes first and the other wave's vector work fills in around it.
-    __builtin_amdgcn_s_setprio(1);
-    f32x16 S[C::NBLK];
-#pragma unroll
-    for (int mb = 0; mb < C::NBLK; ++mb) S[mb] = f32x16{};
-#pragma unroll
+    // Q^T fragments: lane holds query qi, d = ks*16 + 8h .. +7.
+    bf16x8 qf[C::KS];
+  #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < C::NBLK; ++mb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + k_off[ks] + mb * 32 * C::ROWB);
-        S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
-      }
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qi < p.Nq) x = load16(qg + (size_t)qi * D + ks * 16 + 8 * h);
+      x ^= p.qxor;
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
     }
-    // Keep kKDepth K fragment reads in flight ahead of the MFMAs (left alone, the compiler reads two
-    // ahead, and each MFMA pair waits for LDS latency): reads 0..kKDepth-1, then MFMA / read pairs.
-    {
-      constexpr int NK = C::KS * C::NBLK;
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKDepth, 0);
-#pragma unroll
-      for (int i = 0; i < NK - kKDepth; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKDepth, 0);
+
+    int kv_end = nkv;
+    if (CAUSAL) kv_end = min(nkv, q0 + C::BR + p.off);
+    int t_beg = 0, n_tiles = (kv_end + C::BC - 1) / C::BC;  // tiles [t_beg, n_tiles) of this work-group
+    if (SPLIT) {
+      // a paged sequence's own length is cut into S ranges (lengths are only known on the device)
+      const int per = PAGED ? (n_tiles + p.S - 1) / p.S : p.split_tiles;
+      t_beg = min(split * per, n_tiles);
+      n_tiles = min(t_beg + per, n_tiles);
     }
-    // V^T fragments of the whole tile, read now so their LDS latency passes during the softmax; the next
-    // tile's loads go out right after them (+0.7% over the other order)
-    bf16x8 vfr[2 * C::NBLK][C::MBD];
-#pragma unroll
-    for (int kc = 0; kc < 2 * C::NBLK; ++kc)
-#pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd) {
-        const uint8_t* vb = svb + v_off[mbd] + 16 * kc * C::ROWB;
-        const s16x4 lo = lds_read_tr16(vb);
-        const s16x4 hi = lds_read_tr16(vb + 8 * C::ROWB);
-        vfr[kc][mbd] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    // keys this wave needs (0 when the wave's rows lie past N_q)
+    const int wave_kv_end = qw0 >= p.Nq ? 0 : (CAUSAL ? min(nkv, qw0 + 32 + p.off) : nkv);
+    const int lim = CAUSAL ? min(nkv - 1, qi + p.off) : nkv - 1;  // last key this row may attend
+
+    f32x16 oacc[C::MBD];
+  #pragma unroll
+    for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[mbd] = f32x16{};
+    float m_run = kNegInf, l_run = 0.f, lh_run = 0.f;
+
+    // ---------------------------------------------------------------- global -> LDS (direct, no registers)
+    // Load i of wave w fills the 1 KB block (w * LPT + i) of a tile: rows RPL*(w*LPT+i) + lane/CH, physical
+    // chunk lane%CH, which holds logical chunk (lane%CH) ^ swizzle(row).  The per-lane byte offsets within
+    // a tile are fixed; each tile gets a buffer resource starting at its first key and ending at N_kv, so
+    // the loads need no vector address arithmetic and rows past N_kv read zeros (their scores are masked).
+    int ld_k[C::LPT], ld_v[C::LPT];
+  #pragma unroll
+    for (int i = 0; i < C::LPT; ++i) {
+      const int r = C::RPL * (w * C::LPT + i) + lane / C::CH, pc = lane % C::CH;
+      ld_k[i] = r * C::ROWB + 16 * (pc ^ swz_k<D>(r));
+      ld_v[i] = r * C::ROWB + 16 * (pc ^ swz_v<D>(r));
+    }
+    // Paged cache: a 1 KB block (RPL rows, RPL <= 8 <= page size, blocks aligned to RPL) never straddles a
+    // page, so each block gets a descriptor of its own at its page row, spanning the block's rows that lie
+    // before the sequence end, or nothing (zeros land in LDS) when the table entry lies outside the pool.
+    // A tile's 64 keys span at most 64 / page size (<= 8) pages: lane i of every wave loads the tile's i-th
+    // entry (-1 if outside the pool), one tile ahead of the K / V loads that need it, and the blocks read
+    // their entry back with readlane.  absent0/1 hold, per stage, one bit per key of the tile whose entry
+    // lies outside the pool; those keys take the masked path and get zero weight, like keys past the end.
+    uint64_t absent0 = 0, absent1 = 0;
+    int ent_nx = -1;
+    auto fetch_entries = [&](int t) {
+      if constexpr (PAGED) {
+        const int kv0 = t * C::BC, lg = p.lg_page;
+        const int pg0 = kv0 >> lg, n_ent = ((min(kv0 + C::BC, nkv) - 1) >> lg) - pg0 + 1;
+        int e = -1;
+        if (lane < n_ent) e = tab[pg0 + lane];
+        ent_nx = (e >= 0 && e < p.num_pages) ? e : -1;
       }
-    __builtin_amdgcn_sched_barrier(0);
-    next();
-    // mask (diagonal and ragged-tail tiles only; the rest of the tile is one code path)
-    if (masked) {
-      const int rel = lim - kv0 - 4 * h;  // key offset within the tile allowed iff 8*(r/4) + (r%4) + 32*mb <= rel
-      const uint64_t ab = PAGED ? ((STAGE == 0 ? absent0 : absent1) >> (4 * h)) : 0;
-#pragma unroll
-      for (int mb = 0; mb < C::NBLK; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 32 * mb + 8 * (r >> 2) + (r & 3);
-          if (kk > rel || (PAGED && ((ab >> kk) & 1))) S[mb][r] = kNegInf;
+    };
+    auto load_tile = [&](int t, int stage) {
+      const int kv0 = t * C::BC;
+      if constexpr (PAGED) {
+        const int lg = p.lg_page, pmask = (1 << lg) - 1;
+        const int ent = ent_nx;
+        const int n_ent = ((min(kv0 + C::BC, nkv) - 1) >> lg) - (kv0 >> lg) + 1;
+        const uint64_t holes = __builtin_amdgcn_ballot_w64(lane < n_ent && ent < 0);
+        uint64_t bad = 0;
+        if (holes) {
+          if (lg >= 6) {
+            bad = ~0ull;
+          } else {
+            const uint64_t page_keys = (1ull << (1 << lg)) - 1;
+            for (int i = 0; i < n_ent; ++i)
+              if ((holes >> i) & 1) bad |= page_keys << (i << lg);
+          }
         }
+        if (stage == 0)
+          absent0 = bad;
+        else
+          absent1 = bad;
+  #pragma unroll
+        for (int i = 0; i < C::LPT; ++i) {
+          const int rb = C::RPL * (w * C::LPT + i);  // first row of the block within the tile
+          const int r0 = kv0 + rb;
+          const int e = __builtin_amdgcn_readlane(ent, lg >= 6 ? 0 : rb >> lg);
+          int bytes = 0;
+          size_t row_el = 0;
+          if (r0 < nkv && e >= 0) {
+            bytes = min(C::RPL, nkv - r0) * C::ROWB;
+            row_el = ((((size_t)e * p.Hkv) << lg) + (r0 & pmask)) * D;
+          }
+          const int blk = 1024 * (w * C::LPT + i);
+          load16_lds(make_rsrc(kg + row_el, bytes), ld_k[i] - rb * C::ROWB, kbuf(stage) + blk);
+          load16_lds(make_rsrc(vg + row_el, bytes), ld_v[i] - rb * C::ROWB, vbuf(stage) + blk);
+        }
+      } else {
+        const int bytes = (nkv - kv0) * C::ROWB;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
+  #pragma unroll
+        for (int i = 0; i < C::LPT; ++i) {
+          const int blk = 1024 * (w * C::LPT + i);
+          load16_lds(rk, ld_k[i], kbuf(stage) + blk);
+          load16_lds(rv, ld_v[i], vbuf(stage) + blk);
+        }
+      }
+    };
+
+    // ---------------------------------------------------------------- fragment addresses (bytes)
+    // K (A operand of S^T): row 32*mb + l32, logical chunk 2ks + h.
+    int k_off[C::KS];
+  #pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_k<D>(l32));
+    // V^T (A operand of O^T) through ds_read_b64_tr_b16: in lane group G = lane/16 (h = G/2, dh = G%2),
+    // lane j points at row key0 + j/4, d = 32*mbd + 16*dh + 4*(j%4); lane i then receives
+    // V[key0 + t][32*mbd + 16*dh + i], t = 0..3, with key0 = 16*kc + 8*u + 4*h.  The swizzle of those
+    // rows only depends on j/4, so each mbd has one per-lane base and (kc, u) are immediate offsets.
+    const int tr_j = lane & 15, tr_dh = (lane >> 4) & 1, tr_row = 4 * h + tr_j / 4;
+    int v_off[C::MBD];
+  #pragma unroll
+    for (int mbd = 0; mbd < C::MBD; ++mbd) {
+      const int d0 = 32 * mbd + 16 * tr_dh + 4 * (tr_j & 3);
+      v_off[mbd] = tr_row * C::ROWB + 16 * ((d0 >> 3) ^ swz_v<D>(tr_row)) + 2 * (d0 & 7);
     }
-    // Online softmax against the running reference maximum m: the weights are 2^(x - m).  Only the
-    // first tile of a wave (m = -inf) and tiles whose weights would exceed 2^64 reduce the tile's
-    // maximum, move m and rescale O, l; every other tile skips the max reduction (O / l and the LSE do
-    // not depend on which reference is used, and 2^64 keeps every sum far from fp32 overflow).
-    __builtin_amdgcn_s_setprio(0);
-    float rs, rsh;
-    bf16x8 P[2 * C::NBLK];
-    auto weights = [&](float mref) {
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-      rsh = 0.f;
-#pragma unroll
+
+    // ---------------------------------------------------------------- one tile
+    // `next()` issues this wave's loads of the next tile.  It runs right after the S MFMAs are issued, so
+    // the data lands in LDS during the softmax, when the wave reads no fragments (direct LDS writes that
+    // land during the fragment reads of the MFMA phases slow those reads down).
+    auto compute_tile = [&](auto stage_tag, bool masked, int kv0, auto&& next) {
+      constexpr int STAGE = decltype(stage_tag)::value;
+      const uint8_t* sb = kbuf(STAGE);
+      const uint8_t* svb = vbuf(STAGE);
+      // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks).  The wave raises its issue
+      // priority for its MFMA phases and drops it for the softmax, so when both waves of a SIMD are
+      // ready the matrix-core work goes first and the other wave's vector work fills in around it.
+      __builtin_amdgcn_s_setprio(1);
+      f32x16 S[C::NBLK];
+  #pragma unroll
+      for (int mb = 0; mb < C::NBLK; ++mb) S[mb] = f32x16{};
+  #pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+  #pragma unroll
+        for (int mb = 0; mb < C::NBLK; ++mb) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + k_off[ks] + mb * 32 * C::ROWB);
+          S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
+        }
+      }
+      // Keep kKDepth K fragment reads in flight ahead of the MFMAs (left alone, the compiler reads two
+      // ahead, and each MFMA pair waits for LDS latency): reads 0..kKDepth-1, then MFMA / read pairs.
+      {
+        constexpr int NK = C::KS * C::NBLK;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKDepth, 0);
+  #pragma unroll
+        for (int i = 0; i < NK - kKDepth; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKDepth, 0);
+      }
+      // V^T fragments of the whole tile, read now so their LDS latency passes during the softmax; the next
+      // tile's loads go out right after them (+0.7% over the other order)
+      bf16x8 vfr[2 * C::NBLK][C::MBD];
+  #pragma unroll
+      for (int kc = 0; kc < 2 * C::NBLK; ++kc)
+  #pragma unroll
+        for (int mbd = 0; mbd < C::MBD; ++mbd) {
+          const uint8_t* vb = svb + v_off[mbd] + 16 * kc * C::ROWB;
+          const s16x4 lo = lds_read_tr16(vb);
+          const s16x4 hi = lds_read_tr16(vb + 8 * C::ROWB);
+          vfr[kc][mbd] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      next();
+      // mask (diagonal and ragged-tail tiles only; the rest of the tile is one code path)
+      if (masked) {
+        const int rel = lim - kv0 - 4 * h;  // key offset within the tile allowed iff 8*(r/4) + (r%4) + 32*mb <= rel
+        const uint64_t ab = PAGED ? ((STAGE == 0 ? absent0 : absent1) >> (4 * h)) : 0;
+  #pragma unroll
+        for (int mb = 0; mb < C::NBLK; ++mb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 32 * mb + 8 * (r >> 2) + (r & 3);
+            if (kk > rel || (PAGED && ((ab >> kk) & 1))) S[mb][r] = kNegInf;
+          }
+      }
+      // Online softmax against the running reference maximum m: the weights are 2^(x - m).  Only the
+      // first tile of a wave (m = -inf) and tiles whose weights would exceed 2^64 reduce the tile's
+      // maximum, move m and rescale O, l; every other tile skips the max reduction (O / l and the LSE do
+      // not depend on which reference is used, and 2^64 keeps every sum far from fp32 overflow).
+      __builtin_amdgcn_s_setprio(0);
+      float rs, rsh;
+      bf16x8 P[2 * C::NBLK];
+      auto weights = [&](float mref) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        rsh = 0.f;
+  #pragma unroll
+        for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
+          float pr[8];
+  #pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            pr[i] = exp2_hw(fmaf(S[kc >> 1][8 * (kc & 1) + i], c, -mref));
+            part[i & 3] += pr[i];
+          }
+          u32x4 pk;
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+          P[kc] = __builtin_bit_cast(bf16x8, pk);
+          rsh = sum_bf16x8(P[kc], rsh);
+        }
+        rs = (part[0] + part[1]) + (part[2] + part[3]);
+      };
+      bool slow = __builtin_amdgcn_ballot_w64(m_run == kNegInf) != 0;
+      if (!slow) {
+        weights(m_run);
+        slow = __builtin_amdgcn_ballot_w64(!(rs <= kBig)) != 0;  // also true for inf / nan
+      }
+      float alpha = 1.f;
+      if (slow) {
+        float mx = S[0][0];
+  #pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[0][r]);
+  #pragma unroll
+        for (int mb = 1; mb < C::NBLK; ++mb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mb][r]);
+        const float mn = fmaxf(m_run, pair_max(mx) * c);
+        alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - mn);
+        m_run = mn;
+        // a row none of whose keys so far is allowed (possible only inside a key range of a split) keeps
+        // m = -inf and gets zero weights (reference 0 instead of -inf avoids -inf - (-inf))
+        weights(mn == kNegInf ? 0.f : mn);
+  #pragma unroll
+        for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[mbd] *= alpha;
+      }
+      l_run = alpha * l_run + rs;
+      lh_run = alpha * lh_run + rsh;
+      // O^T += V^T P^T, one 16-key chunk at a time across the d blocks (independent accumulators back to
+      // back, so no MFMA waits for the previous one's result)
+      __builtin_amdgcn_s_setprio(1);
+  #pragma unroll
       for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
-        float pr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pr[i] = exp2_hw(fmaf(S[kc >> 1][8 * (kc & 1) + i], c, -mref));
-          part[i & 3] += pr[i];
-        }
-        u32x4 pk;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
-        P[kc] = __builtin_bit_cast(bf16x8, pk);
-        rsh = sum_bf16x8(P[kc], rsh);
+  #pragma unroll
+        for (int mbd = 0; mbd < C::MBD; ++mbd)
+          oacc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[kc][mbd], P[kc], oacc[mbd], 0, 0, 0);
       }
-      rs = (part[0] + part[1]) + (part[2] + part[3]);
     };
-    bool slow = __builtin_amdgcn_ballot_w64(m_run == kNegInf) != 0;
-    if (!slow) {
-      weights(m_run);
-      slow = __builtin_amdgcn_ballot_w64(!(rs <= kBig)) != 0;  // also true for inf / nan
-    }
-    float alpha = 1.f;
-    if (slow) {
-      float mx = S[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[0][r]);
-#pragma unroll
-      for (int mb = 1; mb < C::NBLK; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mb][r]);
-      const float mn = fmaxf(m_run, pair_max(mx) * c);
-      alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - mn);
-      m_run = mn;
-      // a row none of whose keys so far is allowed (possible only inside a key range of a split) keeps
-      // m = -inf and gets zero weights (reference 0 instead of -inf avoids -inf - (-inf))
-      weights(mn == kNegInf ? 0.f : mn);
-#pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd) oacc[mbd] *= alpha;
-    }
-    l_run = alpha * l_run + rs;
-    lh_run = alpha * lh_run + rsh;
-    // O^T += V^T P^T, one 16-key chunk at a time across the d blocks (independent accumulators back to
-    // back, so no MFMA waits for the previous one's result)
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
-#pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd)
-        oacc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[kc][mbd], P[kc], oacc[mbd], 0, 0, 0);
-    }
-  };
 
-  // One loop iteration per tile: wait for this wave's loads of tile t, barrier (now every wave's loads
-  // of tile t have landed and every wave has finished tile t-1, whose stage is reused), start loading
-  // tile t+1, compute tile t.  The loop is unrolled by two so each stage index is a compile-time value.
-  auto tile = [&](auto stage_tag, int t) {
-    constexpr int STAGE = decltype(stage_tag)::value;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const bool more = t + 1 < n_tiles;
-    if (PAGED && more) fetch_entries(t + 1);
-    auto next = [&]() {
-      if (more) load_tile(t + 1, STAGE ^ 1);
+    // One loop iteration per tile: wait for this wave's loads of tile t, barrier (now every wave's loads
+    // of tile t have landed and every wave has finished tile t-1, whose stage is reused), start loading
+    // tile t+1, compute tile t.  The loop is unrolled by two so each stage index is a compile-time value.
+    auto tile = [&](auto stage_tag, int t) {
+      constexpr int STAGE = decltype(stage_tag)::value;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const bool more = t + 1 < n_tiles;
+      if (PAGED && more) fetch_entries(t + 1);
+      auto next = [&]() {
+        if (more) load_tile(t + 1, STAGE ^ 1);
+      };
+      const int kv0 = t * C::BC;
+      const bool holes = PAGED && (STAGE == 0 ? absent0 : absent1) != 0;
+      if (kv0 < wave_kv_end)
+        compute_tile(stage_tag, (kv0 + C::BC > nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off) || holes, kv0, next);
+      else if (more)
+        load_tile(t + 1, STAGE ^ 1);
     };
-    const int kv0 = t * C::BC;
-    const bool holes = PAGED && (STAGE == 0 ? absent0 : absent1) != 0;
-    if (kv0 < wave_kv_end)
-      compute_tile(stage_tag, (kv0 + C::BC > nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off) || holes, kv0, next);
-    else if (more)
-      load_tile(t + 1, STAGE ^ 1);
-  };
 
-  // the two stages alternate from the first tile of the range, so stage = (t - t_beg) & 1
-  if (t_beg < n_tiles) {
-    fetch_entries(t_beg);
-    load_tile(t_beg, 0);
-  }
-  for (int t = t_beg; t < n_tiles; t += 2) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, t + 1);
-  }
+    // the two stages alternate from the first tile of the range, so stage = (t - t_beg) & 1
+    if (t_beg < n_tiles) {
+      fetch_entries(t_beg);
+      load_tile(t_beg, 0);
+    }
+    for (int t = t_beg; t < n_tiles; t += 2) {
+      tile(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, t + 1);
+    }
 
-  // ---------------------------------------------------------------- epilogue
-  // O / l_hat (the weights that entered the value product) rounded to bf16, LSE from the fp32 sum.
-  const float lt = pair_sum(l_run);
-  const float inv = 1.f / pair_sum(lh_run);
-  if (SPLIT) {  // fp32 partial of this key range; a row with no key in it gets O = 0, LSE = -inf
+    // ---------------------------------------------------------------- epilogue
+    // O / l_hat (the weights that entered the value product) rounded to bf16, LSE from the fp32 sum.
+    const float lt = pair_sum(l_run);
+    const float inv = 1.f / pair_sum(lh_run);
+    if (SPLIT) {  // fp32 partial of this key range; a row with no key in it gets O = 0, LSE = -inf
+      if (qi < p.Nq) {
+        const size_t row = (size_t)bh * p.Nq + qi;
+        const bool any = lt > 0.f;
+        float* orow = p.ws_o + (row * p.S + split) * D;
+  #pragma unroll
+        for (int mbd = 0; mbd < C::MBD; ++mbd)
+  #pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 val;
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) val[e] = any ? oacc[mbd][4 * g4 + e] * inv : 0.f;
+            *reinterpret_cast<f32x4*>(orow + mbd * 32 + 8 * g4 + 4 * h) = val;
+          }
+        if (h == 0) p.ws_lse[row * p.S + split] = any ? (m_run + log2_hw(lt)) * kLn2 : kNegInf;
+      }
+      return;
+    }
     if (qi < p.Nq) {
-      const size_t row = (size_t)bh * p.Nq + qi;
-      const bool any = lt > 0.f;
-      float* orow = p.ws_o + (row * p.S + split) * D;
-#pragma unroll
+      uint16_t* orow = p.o + head_q + (size_t)qi * D;
+  #pragma unroll
       for (int mbd = 0; mbd < C::MBD; ++mbd)
-#pragma unroll
+  #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 val;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = any ? oacc[mbd][4 * g4 + e] * inv : 0.f;
-          *reinterpret_cast<f32x4*>(orow + mbd * 32 + 8 * g4 + 4 * h) = val;
+          const f32x16& a = oacc[mbd];
+          u32x2 val;
+          val[0] = pack_bf16x2(a[4 * g4 + 0] * inv, a[4 * g4 + 1] * inv);
+          val[1] = pack_bf16x2(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + mbd * 32 + 8 * g4 + 4 * h) = val;
         }
-      if (h == 0) p.ws_lse[row * p.S + split] = any ? (m_run + log2_hw(lt)) * kLn2 : kNegInf;
+      if (h == 0 && p.lse) p.lse[(size_t)bh * p.Nq + qi] = (m_run + log2_hw(lt)) * kLn2;
     }
-    return;
-  }
-  if (qi < p.Nq) {
-    uint16_t* orow = p.o + head_q + (size_t)qi * D;
-#pragma unroll
-    for (int mbd = 0; mbd < C::MBD; ++mbd)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x16& a = oacc[mbd];
-        u32x2 val;
-        val[0] = pack_bf16x2(a[4 * g4 + 0] * inv, a[4 * g4 + 1] * inv);
-        val[1] = pack_bf16x2(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + mbd * 32 + 8 * g4 + 4 * h) = val;
-      }
-    if (h == 0 && p.lse) p.lse[(size_t)bh * p.Nq + qi] = (m_run + log2_hw(lt)) * kLn2;
   }
 }
 
@@ -513,6 +526,10 @@ static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   int lg = 0;
   while ((1 << lg) < a.page_size) ++lg;
   p.lg_page = lg;
+  // pair causal query tiles when the grid spans at least two work-groups per compute unit (below that
+  // every tile runs at once and pairing would only lengthen the longest chain)
+  p.pair = CAUSAL && !SPLIT && p.n_qt >= 2 && (int64_t)a.B * a.H * p.n_qt >= 2 * kNumCu;
+  if (p.pair) p.total = a.B * a.H * ((p.n_qt + 1) / 2);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, SPLIT, PAGED, NT>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }

@@ -164,6 +164,27 @@ def test_edge_shapes(case):
     check(w, O, L, Oref, Lref)
 
 
+# Causal grids of at least two work-groups per compute unit (B*H*ceil(N_q/128) >= 512) run query tiles in
+# pairs (tile n-1-j, then tile j, in one work-group); every element against the oracle.
+PAIRED = [
+    # B, H, Nq, Nkv, d
+    (1, 74, 1100, 1100, 64),    # 9 tiles per head: four pairs and a lone middle tile; ragged last tile
+    (2, 36, 1000, 1500, 128),   # 8 tiles per head, queries at the end of a longer cache
+    (1, 256, 200, 200, 64),     # exactly 512 work-groups before pairing: tile 1 then tile 0
+    (1, 255, 200, 200, 128),    # 510: just below the threshold, unpaired
+]
+
+
+@pytest.mark.parametrize("case", PAIRED, ids=lambda c: "B{}H{}q{}kv{}d{}".format(*c))
+def test_paired_causal_tiles(case):
+    B, H, Nq, Nkv, d = case
+    w = syn.custom(B, H, Nq, Nkv, d, "bf16", True, None, seed=400 + PAIRED.index(case))
+    host, f64 = inputs(w)
+    O, L = run_fwd(w, host)
+    Oref, Lref = attention_ref(f64["q"], f64["k"], f64["v"], w.scale, w.causal)
+    check(w, O, L, Oref, Lref)
+
+
 def test_identical_keys_give_mean_of_values():
     w = syn.custom(1, 2, 70, 300, 128, "bf16", False, None, seed=3)
     host, f64 = inputs(w)
