@@ -41,6 +41,7 @@ struct BwdParams {
   int Nq, Nkv, off;
   int n_qt, n_kt;            // 128-query / 128-key blocks per (b, h)
   int total_q, total_k;      // work-groups of the two kernels
+  int pair_q, pair_k;        // causal: one work-group runs blocks j and n-1-j (equal work per group)
   float c;                   // scale * log2(e) (any sign)
   float scale;
 };
@@ -121,140 +122,149 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   auto vbuf = [&](int st) -> uint8_t* { return st == 0 ? lv0 : lv1; };
 
   const int lid = xcd_logical_id(blockIdx.x, p.total_q);
-  const int bh = lid / p.n_qt;
-  int qt = lid - bh * p.n_qt;
-  if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query blocks first
-  const int q0 = qt * C::BR;
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l32 = lane & 31, h = lane >> 5;
-  const size_t head_q = (size_t)bh * p.Nq * D, head_kv = (size_t)bh * p.Nkv * D;
-  const uint16_t* __restrict__ kg = p.k + head_kv;
-  const uint16_t* __restrict__ vg = p.v + head_kv;
-  const int qw0 = q0 + 32 * w, qi = qw0 + l32;
-  const bool row_ok = qi < p.Nq;
+  const bool pair = CAUSAL && p.pair_q;
+  const int per_bh = pair ? (p.n_qt + 1) / 2 : p.n_qt;
+  const int bh = lid / per_bh;
+  const int qt_lo = lid - bh * per_bh;
+  const int qt_hi = CAUSAL ? p.n_qt - 1 - qt_lo : qt_lo;  // heaviest query blocks first
+  const int n_pass = (pair && qt_lo != qt_hi) ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+  const int qt = pass == 0 ? qt_hi : qt_lo;
+  if (pass > 0) __syncthreads();  // every wave is done with the LDS stages before they are refilled
+    const int q0 = qt * C::BR;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // lane offsets are recomputed per pass, not held across both
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const size_t head_q = (size_t)bh * p.Nq * D, head_kv = (size_t)bh * p.Nkv * D;
+    const uint16_t* __restrict__ kg = p.k + head_kv;
+    const uint16_t* __restrict__ vg = p.v + head_kv;
+    const int qw0 = q0 + 32 * w, qi = qw0 + l32;
+    const bool row_ok = qi < p.Nq;
 
-  // Q^T and dO^T fragments of this lane's query (d = 16 ks + 8 h .. +7), D_i = dO_i . O_i, LSE_i log2 e
-  bf16x8 qf[C::KS], dof[C::KS];
-  float dpart = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = a, o = a;
-    if (row_ok) {
-      const size_t e = head_q + (size_t)qi * D + ks * 16 + 8 * h;
-      a = load16(p.q + e);
-      b = load16(p.dout + e);
-      o = load16(p.o + e);
+    // Q^T and dO^T fragments of this lane's query (d = 16 ks + 8 h .. +7), D_i = dO_i . O_i, LSE_i log2 e
+    bf16x8 qf[C::KS], dof[C::KS];
+    float dpart = 0.f;
+  #pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = a, o = a;
+      if (row_ok) {
+        const size_t e = head_q + (size_t)qi * D + ks * 16 + 8 * h;
+        a = load16(p.q + e);
+        b = load16(p.dout + e);
+        o = load16(p.o + e);
+      }
+      qf[ks] = __builtin_bit_cast(bf16x8, a);
+      dof[ks] = __builtin_bit_cast(bf16x8, b);
+      dpart += dot8_f32(b, o);
     }
-    qf[ks] = __builtin_bit_cast(bf16x8, a);
-    dof[ks] = __builtin_bit_cast(bf16x8, b);
-    dpart += dot8_f32(b, o);
-  }
-  const float Di = pair_sum(dpart);
-  if (row_ok && h == 0) p.delta[(size_t)bh * p.Nq + qi] = Di;
-  const float lse2 = row_ok ? p.lse[(size_t)bh * p.Nq + qi] * kLog2e : 0.f;
-  const float c = p.c;
+    const float Di = pair_sum(dpart);
+    if (row_ok && h == 0) p.delta[(size_t)bh * p.Nq + qi] = Di;
+    const float lse2 = row_ok ? p.lse[(size_t)bh * p.Nq + qi] * kLog2e : 0.f;
+    const float c = p.c;
 
-  int kv_end = p.Nkv;
-  if (CAUSAL) kv_end = min(p.Nkv, q0 + C::BR + p.off);
-  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
-  const int wave_kv_end = qw0 >= p.Nq ? 0 : (CAUSAL ? min(p.Nkv, qw0 + 32 + p.off) : p.Nkv);
-  const int lim = CAUSAL ? min(p.Nkv - 1, qi + p.off) : p.Nkv - 1;
+    int kv_end = p.Nkv;
+    if (CAUSAL) kv_end = min(p.Nkv, q0 + C::BR + p.off);
+    const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+    const int wave_kv_end = qw0 >= p.Nq ? 0 : (CAUSAL ? min(p.Nkv, qw0 + 32 + p.off) : p.Nkv);
+    const int lim = CAUSAL ? min(p.Nkv - 1, qi + p.off) : p.Nkv - 1;
 
-  f32x16 acc[C::MBD];
-#pragma unroll
-  for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
+    f32x16 acc[C::MBD];
+  #pragma unroll
+    for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
 
-  int ld_off[C::LPT_KV];
-#pragma unroll
-  for (int i = 0; i < C::LPT_KV; ++i) {
-    const int r = C::RPL * (w * C::LPT_KV + i) + lane / C::CH, pc = lane % C::CH;
-    ld_off[i] = r * C::ROWB + 16 * (pc ^ swz_kv<D>(r));
-  }
-  auto load_tile = [&](int t, int stage) {
-    const int kv0 = t * C::BC;
-    const int bytes = (p.Nkv - kv0) * C::ROWB;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
-#pragma unroll
+    int ld_off[C::LPT_KV];
+  #pragma unroll
     for (int i = 0; i < C::LPT_KV; ++i) {
-      const int blk = 1024 * (w * C::LPT_KV + i);
-      load_lds16(rk, ld_off[i], kbuf(stage) + blk);
-      load_lds16(rv, ld_off[i], vbuf(stage) + blk);
+      const int r = C::RPL * (w * C::LPT_KV + i) + lane / C::CH, pc = lane % C::CH;
+      ld_off[i] = r * C::ROWB + 16 * (pc ^ swz_kv<D>(r));
     }
-  };
-  int row_off[C::KS];  // row l32 of a 32-row block, logical chunk 2 ks + h
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) row_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_kv<D>(l32));
-  int trk[C::MBD][2];
-#pragma unroll
-  for (int mbd = 0; mbd < C::MBD; ++mbd) {
-    trk[mbd][0] = tr_offset<D>(lane, mbd, 0);
-    trk[mbd][1] = tr_offset<D>(lane, mbd, 1);
-  }
-
-  auto compute_tile = [&](const uint8_t* kb, const uint8_t* vb, bool masked, int kv0, auto&& next) {
-    f32x16 S[C::NBLK], dP[C::NBLK];
-#pragma unroll
-    for (int mb = 0; mb < C::NBLK; ++mb) S[mb] = dP[mb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < C::NBLK; ++mb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + row_off[ks] + mb * 32 * C::ROWB);
-        S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb + row_off[ks] + mb * 32 * C::ROWB);
-        dP[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[ks], dP[mb], 0, 0, 0);
+    auto load_tile = [&](int t, int stage) {
+      const int kv0 = t * C::BC;
+      const int bytes = (p.Nkv - kv0) * C::ROWB;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
+  #pragma unroll
+      for (int i = 0; i < C::LPT_KV; ++i) {
+        const int blk = 1024 * (w * C::LPT_KV + i);
+        load_lds16(rk, ld_off[i], kbuf(stage) + blk);
+        load_lds16(rv, ld_off[i], vbuf(stage) + blk);
       }
-    next();
-    // dS^T = P^T (dP^T - D), P^T = 2^(s c - LSE log2 e); masked keys get P = 0
-    const int rel = lim - kv0 - 4 * h;
-    bf16x8 dsf[2 * C::NBLK];
-#pragma unroll
-    for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
-      float ds[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * (kc & 1) + i, mb = kc >> 1;
-        float pr = exp2_hw(fmaf(S[mb][r], c, -lse2));
-        if (masked && 32 * mb + 8 * (r >> 2) + (r & 3) > rel) pr = 0.f;
-        ds[i] = pr * (dP[mb][r] - Di);
-      }
-      u32x4 pk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
-      dsf[kc] = __builtin_bit_cast(bf16x8, pk);
-    }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int kc = 0; kc < 2 * C::NBLK; ++kc)
-#pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd)
-        acc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kb + 16 * kc * C::ROWB, trk[mbd]), dsf[kc],
-                                                           acc[mbd], 0, 0, 0);
-  };
-
-  auto tile = [&](auto stage_tag, int t) {
-    constexpr int STAGE = decltype(stage_tag)::value;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const bool more = t + 1 < n_tiles;
-    auto next = [&]() {
-      if (more) load_tile(t + 1, STAGE ^ 1);
     };
-    const int kv0 = t * C::BC;
-    if (kv0 < wave_kv_end)
-      compute_tile(kbuf(STAGE), vbuf(STAGE), (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off),
-                   kv0, next);
-    else if (more)
-      load_tile(t + 1, STAGE ^ 1);
-  };
+    int row_off[C::KS];  // row l32 of a 32-row block, logical chunk 2 ks + h
+  #pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) row_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_kv<D>(l32));
+    int trk[C::MBD][2];
+  #pragma unroll
+    for (int mbd = 0; mbd < C::MBD; ++mbd) {
+      trk[mbd][0] = tr_offset<D>(lane, mbd, 0);
+      trk[mbd][1] = tr_offset<D>(lane, mbd, 1);
+    }
 
-  load_tile(0, 0);
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, t + 1);
+    auto compute_tile = [&](const uint8_t* kb, const uint8_t* vb, bool masked, int kv0, auto&& next) {
+      f32x16 S[C::NBLK], dP[C::NBLK];
+  #pragma unroll
+      for (int mb = 0; mb < C::NBLK; ++mb) S[mb] = dP[mb] = f32x16{};
+  #pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+  #pragma unroll
+        for (int mb = 0; mb < C::NBLK; ++mb) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + row_off[ks] + mb * 32 * C::ROWB);
+          S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb + row_off[ks] + mb * 32 * C::ROWB);
+          dP[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[ks], dP[mb], 0, 0, 0);
+        }
+      next();
+      // dS^T = P^T (dP^T - D), P^T = 2^(s c - LSE log2 e); masked keys get P = 0
+      const int rel = lim - kv0 - 4 * h;
+      bf16x8 dsf[2 * C::NBLK];
+  #pragma unroll
+      for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
+        float ds[8];
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * (kc & 1) + i, mb = kc >> 1;
+          float pr = exp2_hw(fmaf(S[mb][r], c, -lse2));
+          if (masked && 32 * mb + 8 * (r >> 2) + (r & 3) > rel) pr = 0.f;
+          ds[i] = pr * (dP[mb][r] - Di);
+        }
+        u32x4 pk;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+        dsf[kc] = __builtin_bit_cast(bf16x8, pk);
+      }
+      // dQ^T += K^T dS^T
+  #pragma unroll
+      for (int kc = 0; kc < 2 * C::NBLK; ++kc)
+  #pragma unroll
+        for (int mbd = 0; mbd < C::MBD; ++mbd)
+          acc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kb + 16 * kc * C::ROWB, trk[mbd]), dsf[kc],
+                                                             acc[mbd], 0, 0, 0);
+    };
+
+    auto tile = [&](auto stage_tag, int t) {
+      constexpr int STAGE = decltype(stage_tag)::value;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const bool more = t + 1 < n_tiles;
+      auto next = [&]() {
+        if (more) load_tile(t + 1, STAGE ^ 1);
+      };
+      const int kv0 = t * C::BC;
+      if (kv0 < wave_kv_end)
+        compute_tile(kbuf(STAGE), vbuf(STAGE), (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0 + p.off),
+                     kv0, next);
+      else if (more)
+        load_tile(t + 1, STAGE ^ 1);
+    };
+
+    load_tile(0, 0);
+    for (int t = 0; t < n_tiles; t += 2) {
+      tile(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, t + 1);
+    }
+    if (row_ok) store_rowT<D>(p.dq + head_q + (size_t)qi * D, acc, p.scale, h);
   }
-  if (row_ok) store_rowT<D>(p.dq + head_q + (size_t)qi * D, acc, p.scale, h);
 }
 
 // ----------------------------------------------------------------------------------------------- dK, dV
@@ -286,173 +296,183 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   auto dbuf = [&](int st) -> float* { return st == 0 ? ld0 : ld1; };
 
   const int lid = xcd_logical_id(blockIdx.x, p.total_k);
-  const int bh = lid / p.n_kt;
-  const int kt = lid - bh * p.n_kt;  // causal: the first key blocks see the most queries
-  const int k0 = kt * C::BR;
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l32 = lane & 31, h = lane >> 5;
-  const size_t head_q = (size_t)bh * p.Nq * D, head_kv = (size_t)bh * p.Nkv * D;
-  const uint16_t* __restrict__ qg = p.q + head_q;
-  const uint16_t* __restrict__ dog = p.dout + head_q;
-  const int kw0 = k0 + 32 * w, kj = kw0 + l32;
-  const bool key_ok = kj < p.Nkv;
+  const bool pair = CAUSAL && p.pair_k;
+  const int per_bh = pair ? (p.n_kt + 1) / 2 : p.n_kt;
+  const int bh = lid / per_bh;
+  const int kt_hi = lid - bh * per_bh;  // causal: the first key blocks see the most queries
+  const int kt_lo = CAUSAL ? p.n_kt - 1 - kt_hi : kt_hi;
+  const int n_pass = (pair && kt_lo != kt_hi) ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+  const int kt = pass == 0 ? kt_hi : kt_lo;
+  if (pass > 0) __syncthreads();  // every wave is done with the LDS stages and V rows before they are refilled
+    const int k0 = kt * C::BR;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // lane offsets are recomputed per pass, not held across both
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const size_t head_q = (size_t)bh * p.Nq * D, head_kv = (size_t)bh * p.Nkv * D;
+    const uint16_t* __restrict__ qg = p.q + head_q;
+    const uint16_t* __restrict__ dog = p.dout + head_q;
+    const int kw0 = k0 + 32 * w, kj = kw0 + l32;
+    const bool key_ok = kj < p.Nkv;
 
-  // K^T fragments (B operand of S = Q K^T) of this lane's key
-  bf16x8 kf[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u};
-    if (key_ok) a = load16(p.k + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
-    kf[ks] = __builtin_bit_cast(bf16x8, a);
-  }
-  if (WANT_DK) {  // the block's V rows into LDS (rows past N_kv read zeros); visible after the first barrier
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_kv + (size_t)k0 * D, (p.Nkv - k0) * C::ROWB);
-    constexpr int LPV = C::BR * C::ROWB / (C::NT * 16);
-#pragma unroll
-    for (int i = 0; i < LPV; ++i) {
-      const int r = C::RPL * (w * LPV + i) + lane / C::CH, pc = lane % C::CH;
-      load_lds16(rv, r * C::ROWB + 16 * (pc ^ swz_kv<D>(r)), lvk + 1024 * (w * LPV + i));
-    }
-  }
-  const uint8_t* vrow = lvk + 32 * w * C::ROWB;  // this wave's 32 keys
-  const float c = p.c;
-
-  // query tiles: causal blocks start at the first query that may see key k0
-  const int n_qtiles = (p.Nq + C::BQ - 1) / C::BQ;
-  const int t0 = CAUSAL ? max(0, k0 - p.off) / C::BQ : 0;
-  const int wave_q_first = kw0 >= p.Nkv ? p.Nq : (CAUSAL ? max(0, kw0 - p.off) : 0);
-
-  f32x16 acc[C::MBD];                // dV^T (kGradV) or dK^T
-  f32x16 accv[BOTH ? C::MBD : 1];    // dV^T in the fused mode
-#pragma unroll
-  for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
-#pragma unroll
-  for (int mbd = 0; mbd < (BOTH ? C::MBD : 1); ++mbd) accv[mbd] = f32x16{};
-
-  int ld_off[C::LPT_Q];
-#pragma unroll
-  for (int i = 0; i < C::LPT_Q; ++i) {
-    const int r = C::RPL * (w * C::LPT_Q + i) + lane / C::CH, pc = lane % C::CH;
-    ld_off[i] = r * C::ROWB + 16 * (pc ^ swz_kv<D>(r));
-  }
-  auto load_tile = [&](int t, int stage) {
-    const int qr0 = t * C::BQ;
-    const int bytes = (p.Nq - qr0) * C::ROWB;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + (size_t)qr0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dog + (size_t)qr0 * D, bytes);
-#pragma unroll
-    for (int i = 0; i < C::LPT_Q; ++i) {
-      const int blk = 1024 * (w * C::LPT_Q + i);
-      load_lds16(rq, ld_off[i], qbuf(stage) + blk);
-      load_lds16(ro, ld_off[i], obuf(stage) + blk);
-    }
-    if (w == 0 && lane < C::BQ / 4) {  // LSE (and D) of the tile's queries (zeros past N_q)
-      const size_t e = (size_t)bh * p.Nq + qr0;
-      load_lds16(make_rsrc(p.lse + e, (p.Nq - qr0) * 4), 16 * lane, lbuf(stage));
-      if (WANT_DK) load_lds16(make_rsrc(p.delta + e, (p.Nq - qr0) * 4), 16 * lane, dbuf(stage));
-    }
-  };
-  int row_off[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) row_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_kv<D>(l32));
-  int trq[C::MBD][2];
-#pragma unroll
-  for (int mbd = 0; mbd < C::MBD; ++mbd) {
-    trq[mbd][0] = tr_offset<D>(lane, mbd, 0);
-    trq[mbd][1] = tr_offset<D>(lane, mbd, 1);
-  }
-
-  // one 32-query tile: C rows are queries qr0 + 8 g + 4 h + (r & 3), g = r / 4; the lane's column is key kj
-  auto compute_tile = [&](int st, bool masked, int qr0, auto&& next) {
-    const uint8_t* qb = qbuf(st);
-    const uint8_t* ob = obuf(st);
-    f32x16 S = f32x16{}, dP = f32x16{};
-#pragma unroll
+    // K^T fragments (B operand of S = Q K^T) of this lane's key
+    bf16x8 kf[C::KS];
+  #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + row_off[ks]);
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
-      if (WANT_DK) {
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ob + row_off[ks]);
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vrow + row_off[ks]);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dP, 0, 0, 0);
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (key_ok) a = load16(p.k + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
+      kf[ks] = __builtin_bit_cast(bf16x8, a);
+    }
+    if (WANT_DK) {  // the block's V rows into LDS (rows past N_kv read zeros); visible after the first barrier
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_kv + (size_t)k0 * D, (p.Nkv - k0) * C::ROWB);
+      constexpr int LPV = C::BR * C::ROWB / (C::NT * 16);
+  #pragma unroll
+      for (int i = 0; i < LPV; ++i) {
+        const int r = C::RPL * (w * LPV + i) + lane / C::CH, pc = lane % C::CH;
+        load_lds16(rv, r * C::ROWB + 16 * (pc ^ swz_kv<D>(r)), lvk + 1024 * (w * LPV + i));
       }
     }
-    next();
-    const float* lt = lbuf(st);
-    const float* dt = dbuf(st);
-    bf16x8 bf[2];  // P (kGradV) or dS, packed for the B operand
-    bf16x8 bp[2];  // P in the fused mode
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      float x[8], xp[8];
-#pragma unroll
-      for (int g2 = 0; g2 < 2; ++g2) {
-        const int g = 2 * kc + g2;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + 8 * g + 4 * h);
-        f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
-        if (WANT_DK) d4 = *reinterpret_cast<const f32x4*>(dt + 8 * g + 4 * h);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pr = exp2_hw(fmaf(S[r], c, -l4[e] * kLog2e));
-          if (masked && kj > qr0 + 8 * g + 4 * h + e + p.off) pr = 0.f;
-          x[4 * g2 + e] = WANT_DK ? pr * (dP[r] - d4[e]) : pr;
-          xp[4 * g2 + e] = pr;
+    const uint8_t* vrow = lvk + 32 * w * C::ROWB;  // this wave's 32 keys
+    const float c = p.c;
+
+    // query tiles: causal blocks start at the first query that may see key k0
+    const int n_qtiles = (p.Nq + C::BQ - 1) / C::BQ;
+    const int t0 = CAUSAL ? max(0, k0 - p.off) / C::BQ : 0;
+    const int wave_q_first = kw0 >= p.Nkv ? p.Nq : (CAUSAL ? max(0, kw0 - p.off) : 0);
+
+    f32x16 acc[C::MBD];                // dV^T (kGradV) or dK^T
+    f32x16 accv[BOTH ? C::MBD : 1];    // dV^T in the fused mode
+  #pragma unroll
+    for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
+  #pragma unroll
+    for (int mbd = 0; mbd < (BOTH ? C::MBD : 1); ++mbd) accv[mbd] = f32x16{};
+
+    int ld_off[C::LPT_Q];
+  #pragma unroll
+    for (int i = 0; i < C::LPT_Q; ++i) {
+      const int r = C::RPL * (w * C::LPT_Q + i) + lane / C::CH, pc = lane % C::CH;
+      ld_off[i] = r * C::ROWB + 16 * (pc ^ swz_kv<D>(r));
+    }
+    auto load_tile = [&](int t, int stage) {
+      const int qr0 = t * C::BQ;
+      const int bytes = (p.Nq - qr0) * C::ROWB;
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + (size_t)qr0 * D, bytes);
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(dog + (size_t)qr0 * D, bytes);
+  #pragma unroll
+      for (int i = 0; i < C::LPT_Q; ++i) {
+        const int blk = 1024 * (w * C::LPT_Q + i);
+        load_lds16(rq, ld_off[i], qbuf(stage) + blk);
+        load_lds16(ro, ld_off[i], obuf(stage) + blk);
+      }
+      if (w == 0 && lane < C::BQ / 4) {  // LSE (and D) of the tile's queries (zeros past N_q)
+        const size_t e = (size_t)bh * p.Nq + qr0;
+        load_lds16(make_rsrc(p.lse + e, (p.Nq - qr0) * 4), 16 * lane, lbuf(stage));
+        if (WANT_DK) load_lds16(make_rsrc(p.delta + e, (p.Nq - qr0) * 4), 16 * lane, dbuf(stage));
+      }
+    };
+    int row_off[C::KS];
+  #pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) row_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_kv<D>(l32));
+    int trq[C::MBD][2];
+  #pragma unroll
+    for (int mbd = 0; mbd < C::MBD; ++mbd) {
+      trq[mbd][0] = tr_offset<D>(lane, mbd, 0);
+      trq[mbd][1] = tr_offset<D>(lane, mbd, 1);
+    }
+
+    // one 32-query tile: C rows are queries qr0 + 8 g + 4 h + (r & 3), g = r / 4; the lane's column is key kj
+    auto compute_tile = [&](int st, bool masked, int qr0, auto&& next) {
+      const uint8_t* qb = qbuf(st);
+      const uint8_t* ob = obuf(st);
+      f32x16 S = f32x16{}, dP = f32x16{};
+  #pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + row_off[ks]);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
+        if (WANT_DK) {
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ob + row_off[ks]);
+          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vrow + row_off[ks]);
+          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dP, 0, 0, 0);
         }
       }
-      u32x4 pk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-      bf[kc] = __builtin_bit_cast(bf16x8, pk);
-      if constexpr (BOTH) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(xp[2 * i], xp[2 * i + 1]);
-        bp[kc] = __builtin_bit_cast(bf16x8, pk);
+      next();
+      const float* lt = lbuf(st);
+      const float* dt = dbuf(st);
+      bf16x8 bf[2];  // P (kGradV) or dS, packed for the B operand
+      bf16x8 bp[2];  // P in the fused mode
+  #pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        float x[8], xp[8];
+  #pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * kc + g2;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + 8 * g + 4 * h);
+          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+          if (WANT_DK) d4 = *reinterpret_cast<const f32x4*>(dt + 8 * g + 4 * h);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float pr = exp2_hw(fmaf(S[r], c, -l4[e] * kLog2e));
+            if (masked && kj > qr0 + 8 * g + 4 * h + e + p.off) pr = 0.f;
+            x[4 * g2 + e] = WANT_DK ? pr * (dP[r] - d4[e]) : pr;
+            xp[4 * g2 + e] = pr;
+          }
+        }
+        u32x4 pk;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        bf[kc] = __builtin_bit_cast(bf16x8, pk);
+        if constexpr (BOTH) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(xp[2 * i], xp[2 * i + 1]);
+          bp[kc] = __builtin_bit_cast(bf16x8, pk);
+        }
       }
-    }
-    if constexpr (BOTH) {  // dV^T += dO^T P
-#pragma unroll
+      if constexpr (BOTH) {  // dV^T += dO^T P
+  #pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+  #pragma unroll
+          for (int mbd = 0; mbd < C::MBD; ++mbd)
+            accv[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ob + 16 * kc * C::ROWB, trq[mbd]), bp[kc],
+                                                                accv[mbd], 0, 0, 0);
+      }
+      // dV^T += dO^T P  or  dK^T += Q^T dS
+      const uint8_t* ab = WANT_DK ? qb : ob;
+  #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
+  #pragma unroll
         for (int mbd = 0; mbd < C::MBD; ++mbd)
-          accv[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ob + 16 * kc * C::ROWB, trq[mbd]), bp[kc],
-                                                              accv[mbd], 0, 0, 0);
-    }
-    // dV^T += dO^T P  or  dK^T += Q^T dS
-    const uint8_t* ab = WANT_DK ? qb : ob;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int mbd = 0; mbd < C::MBD; ++mbd)
-        acc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ab + 16 * kc * C::ROWB, trq[mbd]), bf[kc],
-                                                           acc[mbd], 0, 0, 0);
-  };
-
-  auto tile = [&](auto stage_tag, int t) {
-    constexpr int STAGE = decltype(stage_tag)::value;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const bool more = t + 1 < n_qtiles;
-    auto next = [&]() {
-      if (more) load_tile(t + 1, STAGE ^ 1);
+          acc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ab + 16 * kc * C::ROWB, trq[mbd]), bf[kc],
+                                                             acc[mbd], 0, 0, 0);
     };
-    const int qr0 = t * C::BQ;
-    if (qr0 + C::BQ - 1 >= wave_q_first)
-      compute_tile(STAGE, CAUSAL && qr0 < kw0 + 31 - p.off, qr0, next);
-    else if (more)
-      load_tile(t + 1, STAGE ^ 1);
-  };
 
-  if (t0 < n_qtiles) load_tile(t0, 0);
-  for (int t = t0; t < n_qtiles; t += 2) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_qtiles) tile(std::integral_constant<int, 1>{}, t + 1);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // every load has landed before the work-group ends (no tile: V rows)
-  if (key_ok) {
-    if (WANT_DK) store_rowT<D>(p.dk + head_kv + (size_t)kj * D, acc, p.scale, h);
-    else store_rowT<D>(p.dv + head_kv + (size_t)kj * D, acc, 1.f, h);
-    if constexpr (BOTH) store_rowT<D>(p.dv + head_kv + (size_t)kj * D, accv, 1.f, h);
+    auto tile = [&](auto stage_tag, int t) {
+      constexpr int STAGE = decltype(stage_tag)::value;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const bool more = t + 1 < n_qtiles;
+      auto next = [&]() {
+        if (more) load_tile(t + 1, STAGE ^ 1);
+      };
+      const int qr0 = t * C::BQ;
+      if (qr0 + C::BQ - 1 >= wave_q_first)
+        compute_tile(STAGE, CAUSAL && qr0 < kw0 + 31 - p.off, qr0, next);
+      else if (more)
+        load_tile(t + 1, STAGE ^ 1);
+    };
+
+    if (t0 < n_qtiles) load_tile(t0, 0);
+    for (int t = t0; t < n_qtiles; t += 2) {
+      tile(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < n_qtiles) tile(std::integral_constant<int, 1>{}, t + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every load has landed before the work-group ends (no tile: V rows)
+    if (key_ok) {
+      if (WANT_DK) store_rowT<D>(p.dk + head_kv + (size_t)kj * D, acc, p.scale, h);
+      else store_rowT<D>(p.dv + head_kv + (size_t)kj * D, acc, 1.f, h);
+      if constexpr (BOTH) store_rowT<D>(p.dv + head_kv + (size_t)kj * D, accv, 1.f, h);
+    }
   }
 }
 
@@ -477,8 +497,12 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   p.off = a.Nkv - a.Nq;
   p.n_qt = (a.Nq + C::BR - 1) / C::BR;
   p.n_kt = (a.Nkv + C::BR - 1) / C::BR;
-  p.total_q = a.B * a.H * p.n_qt;
-  p.total_k = a.B * a.H * p.n_kt;
+  // pair causal blocks when a grid spans at least two work-groups per compute unit (below that every block
+  // runs at once and pairing would only lengthen the longest chain)
+  p.pair_q = CAUSAL && p.n_qt >= 2 && (int64_t)a.B * a.H * p.n_qt >= 2 * kNumCu;
+  p.pair_k = CAUSAL && p.n_kt >= 2 && (int64_t)a.B * a.H * p.n_kt >= 2 * kNumCu;
+  p.total_q = a.B * a.H * (p.pair_q ? (p.n_qt + 1) / 2 : p.n_qt);
+  p.total_k = a.B * a.H * (p.pair_k ? (p.n_kt + 1) / 2 : p.n_kt);
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(p.total_q), dim3(C::NT), 0, s, p);

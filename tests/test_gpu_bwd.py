@@ -75,6 +75,25 @@ def test_bwd_parity(case):
         assert e_fro <= TOL_FRO, f"{name}: {e_fro}"
 
 
+# Causal grids of at least two work-groups per compute unit pair blocks j and n-1-j in one work-group, in
+# both kernels (query blocks for dQ, key blocks for dK / dV).
+PAIRED = [
+    # B, H, Nq, Nkv, d
+    (1, 74, 1100, 1100, 64),    # 9 blocks per head each way: four pairs and a lone middle block; ragged
+    (2, 36, 1000, 1500, 128),   # 8 query blocks, 12 key blocks; queries at the end of a longer cache
+    (1, 256, 200, 200, 64),     # exactly 512 work-groups per kernel before pairing
+]
+
+
+@pytest.mark.parametrize("case", PAIRED, ids=lambda c: "B{}H{}q{}kv{}d{}".format(*c))
+def test_bwd_paired_blocks(case):
+    B, H, Nq, Nkv, d = case
+    out = run_case(B, H, Nq, Nkv, d, True, None, seed=450 + PAIRED.index(case))
+    for name, (e_max, e_fro, g, r) in out.items():
+        assert e_max <= TOL_MAX, f"{name}: {e_max}"
+        assert e_fro <= TOL_FRO, f"{name}: {e_fro}"
+
+
 def dq_rounding_bound(q, k, v, do, scale, causal):
     """First-order bound on |dQ_gpu - dQ_exact| from the bf16 roundings the backward takes by design
     (unit roundoff u = 2^-8): dS rounded for the dQ product, D = rowsum(dO * O) from the bf16 forward
