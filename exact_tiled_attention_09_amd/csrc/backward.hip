@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     // Q^T and dO^T fragments of this lane's query (d = 16 ks + 8 h .. +7), D_i = dO_i . O_i, LSE_i log2 e
     bf16x8 qf[C::KS], dof[C::KS];
     float dpart = 0.f;
-  #pragma unroll
+#pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 a = {0u, 0u, 0u, 0u}, b = a, o = a;
       if (row_ok) {
@@ -170,11 +170,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     const int lim = CAUSAL ? min(p.Nkv - 1, qi + p.off) : p.Nkv - 1;
 
     f32x16 acc[C::MBD];
-  #pragma unroll
+#pragma unroll
     for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
 
     int ld_off[C::LPT_KV];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < C::LPT_KV; ++i) {
       const int r = C::RPL * (w * C::LPT_KV + i) + lane / C::CH, pc = lane % C::CH;
       ld_off[i] = r * C::ROWB + 16 * (pc ^ swz_kv<D>(r));
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       const int bytes = (p.Nkv - kv0) * C::ROWB;
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)kv0 * D, bytes);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)kv0 * D, bytes);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < C::LPT_KV; ++i) {
         const int blk = 1024 * (w * C::LPT_KV + i);
         load_lds16(rk, ld_off[i], kbuf(stage) + blk);
@@ -192,10 +192,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       }
     };
     int row_off[C::KS];  // row l32 of a 32-row block, logical chunk 2 ks + h
-  #pragma unroll
+#pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) row_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_kv<D>(l32));
     int trk[C::MBD][2];
-  #pragma unroll
+#pragma unroll
     for (int mbd = 0; mbd < C::MBD; ++mbd) {
       trk[mbd][0] = tr_offset<D>(lane, mbd, 0);
       trk[mbd][1] = tr_offset<D>(lane, mbd, 1);
@@ -203,11 +203,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
     auto compute_tile = [&](const uint8_t* kb, const uint8_t* vb, bool masked, int kv0, auto&& next) {
       f32x16 S[C::NBLK], dP[C::NBLK];
-  #pragma unroll
+#pragma unroll
       for (int mb = 0; mb < C::NBLK; ++mb) S[mb] = dP[mb] = f32x16{};
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-  #pragma unroll
+#pragma unroll
         for (int mb = 0; mb < C::NBLK; ++mb) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + row_off[ks] + mb * 32 * C::ROWB);
           S[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[mb], 0, 0, 0);
@@ -218,10 +218,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       // dS^T = P^T (dP^T - D), P^T = 2^(s c - LSE log2 e); masked keys get P = 0
       const int rel = lim - kv0 - 4 * h;
       bf16x8 dsf[2 * C::NBLK];
-  #pragma unroll
+#pragma unroll
       for (int kc = 0; kc < 2 * C::NBLK; ++kc) {
         float ds[8];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * (kc & 1) + i, mb = kc >> 1;
           float pr = exp2_hw(fmaf(S[mb][r], c, -lse2));
@@ -229,14 +229,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
           ds[i] = pr * (dP[mb][r] - Di);
         }
         u32x4 pk;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
         dsf[kc] = __builtin_bit_cast(bf16x8, pk);
       }
       // dQ^T += K^T dS^T
-  #pragma unroll
+#pragma unroll
       for (int kc = 0; kc < 2 * C::NBLK; ++kc)
-  #pragma unroll
+#pragma unroll
         for (int mbd = 0; mbd < C::MBD; ++mbd)
           acc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kb + 16 * kc * C::ROWB, trk[mbd]), dsf[kc],
                                                              acc[mbd], 0, 0, 0);
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
 
     // K^T fragments (B operand of S = Q K^T) of this lane's key
     bf16x8 kf[C::KS];
-  #pragma unroll
+#pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 a = {0u, 0u, 0u, 0u};
       if (key_ok) a = load16(p.k + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     if (WANT_DK) {  // the block's V rows into LDS (rows past N_kv read zeros); visible after the first barrier
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_kv + (size_t)k0 * D, (p.Nkv - k0) * C::ROWB);
       constexpr int LPV = C::BR * C::ROWB / (C::NT * 16);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < LPV; ++i) {
         const int r = C::RPL * (w * LPV + i) + lane / C::CH, pc = lane % C::CH;
         load_lds16(rv, r * C::ROWB + 16 * (pc ^ swz_kv<D>(r)), lvk + 1024 * (w * LPV + i));
@@ -343,13 +343,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
 
     f32x16 acc[C::MBD];                // dV^T (kGradV) or dK^T
     f32x16 accv[BOTH ? C::MBD : 1];    // dV^T in the fused mode
-  #pragma unroll
+#pragma unroll
     for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
-  #pragma unroll
+#pragma unroll
     for (int mbd = 0; mbd < (BOTH ? C::MBD : 1); ++mbd) accv[mbd] = f32x16{};
 
     int ld_off[C::LPT_Q];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < C::LPT_Q; ++i) {
       const int r = C::RPL * (w * C::LPT_Q + i) + lane / C::CH, pc = lane % C::CH;
       ld_off[i] = r * C::ROWB + 16 * (pc ^ swz_kv<D>(r));
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       const int bytes = (p.Nq - qr0) * C::ROWB;
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + (size_t)qr0 * D, bytes);
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(dog + (size_t)qr0 * D, bytes);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < C::LPT_Q; ++i) {
         const int blk = 1024 * (w * C::LPT_Q + i);
         load_lds16(rq, ld_off[i], qbuf(stage) + blk);
@@ -372,10 +372,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       }
     };
     int row_off[C::KS];
-  #pragma unroll
+#pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) row_off[ks] = l32 * C::ROWB + 16 * ((2 * ks + h) ^ swz_kv<D>(l32));
     int trq[C::MBD][2];
-  #pragma unroll
+#pragma unroll
     for (int mbd = 0; mbd < C::MBD; ++mbd) {
       trq[mbd][0] = tr_offset<D>(lane, mbd, 0);
       trq[mbd][1] = tr_offset<D>(lane, mbd, 1);
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       const uint8_t* qb = qbuf(st);
       const uint8_t* ob = obuf(st);
       f32x16 S = f32x16{}, dP = f32x16{};
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + row_off[ks]);
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
@@ -401,16 +401,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       const float* dt = dbuf(st);
       bf16x8 bf[2];  // P (kGradV) or dS, packed for the B operand
       bf16x8 bp[2];  // P in the fused mode
-  #pragma unroll
+#pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         float x[8], xp[8];
-  #pragma unroll
+#pragma unroll
         for (int g2 = 0; g2 < 2; ++g2) {
           const int g = 2 * kc + g2;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + 8 * g + 4 * h);
           f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
           if (WANT_DK) d4 = *reinterpret_cast<const f32x4*>(dt + 8 * g + 4 * h);
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             float pr = exp2_hw(fmaf(S[r], c, -l4[e] * kLog2e));
@@ -420,28 +420,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
           }
         }
         u32x4 pk;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
         bf[kc] = __builtin_bit_cast(bf16x8, pk);
         if constexpr (BOTH) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(xp[2 * i], xp[2 * i + 1]);
           bp[kc] = __builtin_bit_cast(bf16x8, pk);
         }
       }
       if constexpr (BOTH) {  // dV^T += dO^T P
-  #pragma unroll
+#pragma unroll
         for (int kc = 0; kc < 2; ++kc)
-  #pragma unroll
+#pragma unroll
           for (int mbd = 0; mbd < C::MBD; ++mbd)
             accv[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ob + 16 * kc * C::ROWB, trq[mbd]), bp[kc],
                                                                 accv[mbd], 0, 0, 0);
       }
       // dV^T += dO^T P  or  dK^T += Q^T dS
       const uint8_t* ab = WANT_DK ? qb : ob;
-  #pragma unroll
+#pragma unroll
       for (int kc = 0; kc < 2; ++kc)
-  #pragma unroll
+#pragma unroll
         for (int mbd = 0; mbd < C::MBD; ++mbd)
           acc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ab + 16 * kc * C::ROWB, trq[mbd]), bf[kc],
                                                              acc[mbd], 0, 0, 0);
