@@ -15,10 +15,11 @@
 //    Per 64-key tile: S^T = K Q^T and dP^T = V dO^T (K, V fragments from LDS), dS^T in registers,
 //    dQ^T += K^T dS^T (K^T through ds_read_b64_tr_b16 of the same K tile).
 //  * bwd_dkdv_kernel: one work-group per (b, h, 128 keys), the same layout with the roles of queries and
-//    keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query tile streamed through LDS:
-//    S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through transposing
-//    reads).  At d = 64 one pass forms both; at d = 128 both accumulators do not fit beside the rest at
-//    two waves per SIMD, so a dV pass and a dK pass run one after the other.
+//    keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query block of the tiles streamed
+//    through LDS (64 queries per tile, 32 in the dK pass whose V rows also take LDS): S = Q K^T,
+//    dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through transposing reads).  At
+//    d = 64 one pass forms both; at d = 128 both accumulators do not fit beside the rest at two waves per
+//    SIMD, so a dV pass and a dK pass run one after the other.
 // Tiles read both row-wise (ds_read_b128) and transposed (ds_read_b64_tr_b16) use a swizzle that keeps
 // both access patterns on distinct banks.
 #include "common.h"
@@ -51,12 +52,11 @@ struct BwdCfg {
   static constexpr int NW = 4, NT = 256;
   static constexpr int BR = 128;           // queries (dQ kernel) or keys (dK/dV kernel) per work-group
   static constexpr int BC = 64;            // keys per tile in the dQ kernel
-  static constexpr int BQ = 32;            // queries per tile in the dK/dV kernel
   static constexpr int ROWB = 2 * D, CH = D / 8, KS = D / 16, MBD = D / 32, RPL = 1024 / ROWB;
   static constexpr int NBLK = BC / 32;
-  static constexpr int TKV = BC * ROWB, TQ = BQ * ROWB;
-  static constexpr int LPT_KV = TKV / (NT * 16), LPT_Q = TQ / (NT * 16);
-  static_assert(TKV % (NT * 16) == 0 && TQ % (NT * 16) == 0, "tile loads must divide evenly");
+  static constexpr int TKV = BC * ROWB;
+  static constexpr int LPT_KV = TKV / (NT * 16);
+  static_assert(TKV % (NT * 16) == 0 && 32 * ROWB % (NT * 16) == 0, "tile loads must divide evenly");
 };
 
 // Row swizzle (16-byte chunk XOR) for tiles that are read both as MFMA rows (32 lanes, 32 rows, one
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const int qt_hi = CAUSAL ? p.n_qt - 1 - qt_lo : qt_lo;  // heaviest query blocks first
   const int n_pass = (pair && qt_lo != qt_hi) ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
-  const int qt = pass == 0 ? qt_hi : qt_lo;
-  if (pass > 0) __syncthreads();  // every wave is done with the LDS stages before they are refilled
+    const int qt = pass == 0 ? qt_hi : qt_lo;
+    if (pass > 0) __syncthreads();  // every wave is done with the LDS stages before they are refilled
     const int q0 = qt * C::BR;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));  // lane offsets are recomputed per pass, not held across both
@@ -286,8 +286,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr bool WANT_DK = MODE != kGradV;  // dP, dS and the V rows are needed
   constexpr bool BOTH = MODE == kGradKV;
   static_assert(!BOTH || D == 64, "the fused mode fits the register budget at d = 64 only");
-  __shared__ __attribute__((aligned(16))) uint8_t lq0[C::TQ], ldo0[C::TQ], lq1[C::TQ], ldo1[C::TQ];
-  __shared__ __attribute__((aligned(16))) float ll0[C::BQ], ld0[C::BQ], ll1[C::BQ], ld1[C::BQ];
+  // queries per streamed tile: 64 (two 32-query blocks per barrier) unless the dK pass's V rows must fit too
+  constexpr int BQT = MODE == kGradK ? 32 : 64, NSB = BQT / 32;
+  constexpr int TQT = BQT * C::ROWB, LPT = TQT / (C::NT * 16);
+  __shared__ __attribute__((aligned(16))) uint8_t lq0[TQT], ldo0[TQT], lq1[TQT], ldo1[TQT];
+  __shared__ __attribute__((aligned(16))) float ll0[BQT], ld0[BQT], ll1[BQT], ld1[BQT];
   // V of the work-group's 128 keys (B operand of dP = dO V^T; not needed by the dV pass)
   __shared__ __attribute__((aligned(16))) uint8_t lvk[WANT_DK ? C::BR * C::ROWB : 16];
   auto qbuf = [&](int st) -> uint8_t* { return st == 0 ? lq0 : lq1; };
@@ -303,8 +306,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   const int kt_lo = CAUSAL ? p.n_kt - 1 - kt_hi : kt_hi;
   const int n_pass = (pair && kt_lo != kt_hi) ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
-  const int kt = pass == 0 ? kt_hi : kt_lo;
-  if (pass > 0) __syncthreads();  // every wave is done with the LDS stages and V rows before they are refilled
+    const int kt = pass == 0 ? kt_hi : kt_lo;
+    if (pass > 0) __syncthreads();  // every wave is done with the LDS stages and V rows before refilling
     const int k0 = kt * C::BR;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));  // lane offsets are recomputed per pass, not held across both
@@ -337,8 +340,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     const float c = p.c;
 
     // query tiles: causal blocks start at the first query that may see key k0
-    const int n_qtiles = (p.Nq + C::BQ - 1) / C::BQ;
-    const int t0 = CAUSAL ? max(0, k0 - p.off) / C::BQ : 0;
+    const int n_qtiles = (p.Nq + BQT - 1) / BQT;
+    const int t0 = CAUSAL ? max(0, k0 - p.off) / BQT : 0;
     const int wave_q_first = kw0 >= p.Nkv ? p.Nq : (CAUSAL ? max(0, kw0 - p.off) : 0);
 
     f32x16 acc[C::MBD];                // dV^T (kGradV) or dK^T
@@ -348,24 +351,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int mbd = 0; mbd < (BOTH ? C::MBD : 1); ++mbd) accv[mbd] = f32x16{};
 
-    int ld_off[C::LPT_Q];
+    int ld_off[LPT];
 #pragma unroll
-    for (int i = 0; i < C::LPT_Q; ++i) {
-      const int r = C::RPL * (w * C::LPT_Q + i) + lane / C::CH, pc = lane % C::CH;
+    for (int i = 0; i < LPT; ++i) {
+      const int r = C::RPL * (w * LPT + i) + lane / C::CH, pc = lane % C::CH;
       ld_off[i] = r * C::ROWB + 16 * (pc ^ swz_kv<D>(r));
     }
     auto load_tile = [&](int t, int stage) {
-      const int qr0 = t * C::BQ;
+      const int qr0 = t * BQT;
       const int bytes = (p.Nq - qr0) * C::ROWB;
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + (size_t)qr0 * D, bytes);
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(dog + (size_t)qr0 * D, bytes);
 #pragma unroll
-      for (int i = 0; i < C::LPT_Q; ++i) {
-        const int blk = 1024 * (w * C::LPT_Q + i);
+      for (int i = 0; i < LPT; ++i) {
+        const int blk = 1024 * (w * LPT + i);
         load_lds16(rq, ld_off[i], qbuf(stage) + blk);
         load_lds16(ro, ld_off[i], obuf(stage) + blk);
       }
-      if (w == 0 && lane < C::BQ / 4) {  // LSE (and D) of the tile's queries (zeros past N_q)
+      if (w == 0 && lane < BQT / 4) {  // LSE (and D) of the tile's queries (zeros past N_q)
         const size_t e = (size_t)bh * p.Nq + qr0;
         load_lds16(make_rsrc(p.lse + e, (p.Nq - qr0) * 4), 16 * lane, lbuf(stage));
         if (WANT_DK) load_lds16(make_rsrc(p.delta + e, (p.Nq - qr0) * 4), 16 * lane, dbuf(stage));
@@ -381,10 +384,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       trq[mbd][1] = tr_offset<D>(lane, mbd, 1);
     }
 
-    // one 32-query tile: C rows are queries qr0 + 8 g + 4 h + (r & 3), g = r / 4; the lane's column is key kj
-    auto compute_tile = [&](int st, bool masked, int qr0, auto&& next) {
-      const uint8_t* qb = qbuf(st);
-      const uint8_t* ob = obuf(st);
+    // one 32-query block at row 32 sb of the tile: C rows are queries qr0 + 8 g + 4 h + (r & 3), g = r / 4;
+    // the lane's column is key kj
+    auto compute_block = [&](int st, int sb, bool masked, int qr0, bool first, auto&& next) {
+      const uint8_t* qb = qbuf(st) + 32 * sb * C::ROWB;
+      const uint8_t* ob = obuf(st) + 32 * sb * C::ROWB;
       f32x16 S = f32x16{}, dP = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
@@ -396,9 +400,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
           dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dP, 0, 0, 0);
         }
       }
-      next();
-      const float* lt = lbuf(st);
-      const float* dt = dbuf(st);
+      if (first) next();
+      const float* lt = lbuf(st) + 32 * sb;
+      const float* dt = dbuf(st) + 32 * sb;
       bf16x8 bf[2];  // P (kGradV) or dS, packed for the B operand
       bf16x8 bp[2];  // P in the fused mode
 #pragma unroll
@@ -455,11 +459,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       auto next = [&]() {
         if (more) load_tile(t + 1, STAGE ^ 1);
       };
-      const int qr0 = t * C::BQ;
-      if (qr0 + C::BQ - 1 >= wave_q_first)
-        compute_tile(STAGE, CAUSAL && qr0 < kw0 + 31 - p.off, qr0, next);
-      else if (more)
-        load_tile(t + 1, STAGE ^ 1);
+      const int qr0 = t * BQT;
+      bool first = true;  // the next tile's loads go out after the first computed block's score MFMAs
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int qb0 = qr0 + 32 * sb;
+        if (qb0 + 31 < wave_q_first) continue;  // every query of the block precedes the wave's keys
+        compute_block(STAGE, sb, CAUSAL && qb0 < kw0 + 31 - p.off, qb0, first, next);
+        first = false;
+      }
+      if (first) next();
     };
 
     if (t0 < n_qtiles) load_tile(t0, 0);
