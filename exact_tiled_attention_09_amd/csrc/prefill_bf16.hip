@@ -27,7 +27,8 @@
 //  * K and V tiles of 64 keys go global -> LDS with direct 16-byte loads (buffer_load_dwordx4 ... lds,
 //    no staging registers), double-buffered with one barrier per tile: tile t+1 is in flight while
 //    tile t is computed.  The loads of tile t+1 are issued right after the S MFMAs of tile t (and the
-//    V^T fragment reads), so they land during the softmax rather than during fragment reads.  16-byte chunks are XOR-swizzled within
+//    V^T fragment reads), so they land during the softmax rather than during fragment reads; decode-like
+//    launches (NT, below) issue them at the top of the tile.  16-byte chunks are XOR-swizzled within
 //    each row (the swizzle is applied through each lane's source address) so every fragment read hits
 //    distinct banks, and fragment addresses are per-lane bases plus compile-time offsets.
 //  * Fragment reads run ahead of their MFMAs: K fragments four deep (scheduling groups), and all V^T
@@ -35,7 +36,8 @@
 //  * Causal tiles above the diagonal are never loaded; a wave skips the math of tiles that lie fully
 //    above its rows; only diagonal and ragged-tail tiles evaluate the mask.
 //  * Work-group ids are remapped so each XCD walks contiguous (head, tile) ranges, heaviest causal
-//    query tiles first.
+//    query tiles first.  Causal grids of at least two work-groups per CU pair query tiles n-1-j and j in
+//    one work-group (two passes over the same code), so every work-group carries the same load.
 // Modes (template flags): SPLIT cuts each query tile's keys into S ranges of whole tiles, one
 // work-group each, and writes fp32 partials (O_s normalised, LSE_s) that the decode combine merges; it
 // serves short query chunks against a long cache and grouped-head decode (the G query heads of a
