@@ -15,11 +15,9 @@
 //    Per 64-key tile: S^T = K Q^T and dP^T = V dO^T (K, V fragments from LDS), dS^T in registers,
 //    dQ^T += K^T dS^T (K^T through ds_read_b64_tr_b16 of the same K tile).
 //  * bwd_dkdv_kernel: one work-group per (b, h, 128 keys), the same layout with the roles of queries and
-//    keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query block of the tiles streamed
-//    through LDS (64 queries per tile, 32 in the dK pass whose V rows also take LDS): S = Q K^T,
-//    dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through transposing reads).  At
-//    d = 64 one pass forms both; at d = 128 both accumulators do not fit beside the rest at two waves per
-//    SIMD, so a dV pass and a dK pass run one after the other.
+//    keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query block of the 64-query tiles
+//    streamed through LDS: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T
+//    through transposing reads), both gradients in one pass.
 // Tiles read both row-wise (ds_read_b128) and transposed (ds_read_b64_tr_b16) use a swizzle that keeps
 // both access patterns on distinct banks.
 #include "common.h"
@@ -269,30 +267,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------------------------------------- dK, dV
 
-// Which gradients one bwd_dkdv_kernel launch forms.
-enum BwdKvMode : int {
-  kGradV = 0,   // S, P, dV^T += dO^T P
-  kGradK = 1,   // S, dP, dS, dK^T += Q^T dS
-  kGradKV = 2,  // both from one S and dP
-};
-
-// One kernel body for the three modes.  The fused mode saves recomputing S and re-streaming Q, dO
-// (D/4 MFMAs per 32x32 key-query block instead of 5 D/16) but holds both D x 32 accumulators: at
-// d = 128 that needs more than the 256 registers of two waves per SIMD, and at one wave per SIMD it was
-// slower than the two passes, so d = 128 runs kGradV then kGradK.
-template <int D, bool CAUSAL, int MODE>
+// One pass forms both gradients from one S and dP per 32x32 key-query block (D/4 MFMAs; two separate
+// dV and dK passes would need 5 D/16 and stream Q, dO twice).  It holds both D x 32 accumulators: at
+// d = 128 the wave's V fragments live in registers next to its K fragments (V rows in LDS would leave
+// one work-group per CU), and the compiler spills a few of those fragments to scratch, reloaded once per
+// block; that still ran 5% faster than the two passes at B1 H32 N8192.  At d = 64 the block's V rows sit
+// in LDS and everything fits at three waves per SIMD.
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  constexpr bool WANT_DK = MODE != kGradV;  // dP, dS and the V rows are needed
-  constexpr bool BOTH = MODE == kGradKV;
-  static_assert(!BOTH || D == 64, "the fused mode fits the register budget at d = 64 only");
-  // queries per streamed tile: 64 (two 32-query blocks per barrier) unless the dK pass's V rows must fit too
-  constexpr int BQT = MODE == kGradK ? 32 : 64, NSB = BQT / 32;
+  constexpr bool VREG = D == 128;  // V fragments of the wave's keys in registers instead of LDS
+  // 64 queries per streamed tile: two 32-query blocks per barrier
+  constexpr int BQT = 64, NSB = BQT / 32;
   constexpr int TQT = BQT * C::ROWB, LPT = TQT / (C::NT * 16);
   __shared__ __attribute__((aligned(16))) uint8_t lq0[TQT], ldo0[TQT], lq1[TQT], ldo1[TQT];
   __shared__ __attribute__((aligned(16))) float ll0[BQT], ld0[BQT], ll1[BQT], ld1[BQT];
-  // V of the work-group's 128 keys (B operand of dP = dO V^T; not needed by the dV pass)
-  __shared__ __attribute__((aligned(16))) uint8_t lvk[WANT_DK ? C::BR * C::ROWB : 16];
+  // V of the work-group's 128 keys (B operand of dP = dO V^T) when it is not held in registers
+  __shared__ __attribute__((aligned(16))) uint8_t lvk[VREG ? 16 : C::BR * C::ROWB];
   auto qbuf = [&](int st) -> uint8_t* { return st == 0 ? lq0 : lq1; };
   auto obuf = [&](int st) -> uint8_t* { return st == 0 ? ldo0 : ldo1; };
   auto lbuf = [&](int st) -> float* { return st == 0 ? ll0 : ll1; };
@@ -319,15 +310,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     const int kw0 = k0 + 32 * w, kj = kw0 + l32;
     const bool key_ok = kj < p.Nkv;
 
-    // K^T fragments (B operand of S = Q K^T) of this lane's key
-    bf16x8 kf[C::KS];
+    // K^T and (d = 128) V^T fragments of this lane's key: B operands of S = Q K^T and dP = dO V^T
+    bf16x8 kf[C::KS], vf[VREG ? C::KS : 1];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 a = {0u, 0u, 0u, 0u};
-      if (key_ok) a = load16(p.k + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
+      u32x4 a = {0u, 0u, 0u, 0u}, b = a;
+      if (key_ok) {
+        a = load16(p.k + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
+        if (VREG) b = load16(p.v + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
+      }
       kf[ks] = __builtin_bit_cast(bf16x8, a);
+      if constexpr (VREG) vf[ks] = __builtin_bit_cast(bf16x8, b);
     }
-    if (WANT_DK) {  // the block's V rows into LDS (rows past N_kv read zeros); visible after the first barrier
+    if constexpr (!VREG) {  // the block's V rows into LDS (rows past N_kv read zeros); visible after the first barrier
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_kv + (size_t)k0 * D, (p.Nkv - k0) * C::ROWB);
       constexpr int LPV = C::BR * C::ROWB / (C::NT * 16);
 #pragma unroll
@@ -344,12 +339,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     const int t0 = CAUSAL ? max(0, k0 - p.off) / BQT : 0;
     const int wave_q_first = kw0 >= p.Nkv ? p.Nq : (CAUSAL ? max(0, kw0 - p.off) : 0);
 
-    f32x16 acc[C::MBD];                // dV^T (kGradV) or dK^T
-    f32x16 accv[BOTH ? C::MBD : 1];    // dV^T in the fused mode
+    f32x16 acck[C::MBD], accv[C::MBD];  // dK^T, dV^T
 #pragma unroll
-    for (int mbd = 0; mbd < C::MBD; ++mbd) acc[mbd] = f32x16{};
-#pragma unroll
-    for (int mbd = 0; mbd < (BOTH ? C::MBD : 1); ++mbd) accv[mbd] = f32x16{};
+    for (int mbd = 0; mbd < C::MBD; ++mbd) acck[mbd] = accv[mbd] = f32x16{};
 
     int ld_off[LPT];
 #pragma unroll
@@ -368,10 +360,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
         load_lds16(rq, ld_off[i], qbuf(stage) + blk);
         load_lds16(ro, ld_off[i], obuf(stage) + blk);
       }
-      if (w == 0 && lane < BQT / 4) {  // LSE (and D) of the tile's queries (zeros past N_q)
+      if (w == 0 && lane < BQT / 4) {  // LSE and D of the tile's queries (zeros past N_q)
         const size_t e = (size_t)bh * p.Nq + qr0;
         load_lds16(make_rsrc(p.lse + e, (p.Nq - qr0) * 4), 16 * lane, lbuf(stage));
-        if (WANT_DK) load_lds16(make_rsrc(p.delta + e, (p.Nq - qr0) * 4), 16 * lane, dbuf(stage));
+        load_lds16(make_rsrc(p.delta + e, (p.Nq - qr0) * 4), 16 * lane, dbuf(stage));
       }
     };
     int row_off[C::KS];
@@ -394,61 +386,54 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       for (int ks = 0; ks < C::KS; ++ks) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + row_off[ks]);
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
-        if (WANT_DK) {
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ob + row_off[ks]);
-          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vrow + row_off[ks]);
-          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dP, 0, 0, 0);
-        }
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ob + row_off[ks]);
+        bf16x8 vb;
+        if constexpr (VREG) vb = vf[ks];
+        else vb = *reinterpret_cast<const bf16x8*>(vrow + row_off[ks]);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dP, 0, 0, 0);
       }
       if (first) next();
       const float* lt = lbuf(st) + 32 * sb;
       const float* dt = dbuf(st) + 32 * sb;
-      bf16x8 bf[2];  // P (kGradV) or dS, packed for the B operand
-      bf16x8 bp[2];  // P in the fused mode
+      bf16x8 bs[2], bp[2];  // dS and P, packed for the B operand
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        float x[8], xp[8];
+        float xs[8], xp[8];
 #pragma unroll
         for (int g2 = 0; g2 < 2; ++g2) {
           const int g = 2 * kc + g2;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + 8 * g + 4 * h);
-          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
-          if (WANT_DK) d4 = *reinterpret_cast<const f32x4*>(dt + 8 * g + 4 * h);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + 8 * g + 4 * h);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             float pr = exp2_hw(fmaf(S[r], c, -l4[e] * kLog2e));
             if (masked && kj > qr0 + 8 * g + 4 * h + e + p.off) pr = 0.f;
-            x[4 * g2 + e] = WANT_DK ? pr * (dP[r] - d4[e]) : pr;
+            xs[4 * g2 + e] = pr * (dP[r] - d4[e]);
             xp[4 * g2 + e] = pr;
           }
         }
         u32x4 pk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-        bf[kc] = __builtin_bit_cast(bf16x8, pk);
-        if constexpr (BOTH) {
+        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(xs[2 * i], xs[2 * i + 1]);
+        bs[kc] = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(xp[2 * i], xp[2 * i + 1]);
-          bp[kc] = __builtin_bit_cast(bf16x8, pk);
-        }
+        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(xp[2 * i], xp[2 * i + 1]);
+        bp[kc] = __builtin_bit_cast(bf16x8, pk);
       }
-      if constexpr (BOTH) {  // dV^T += dO^T P
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-          for (int mbd = 0; mbd < C::MBD; ++mbd)
-            accv[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ob + 16 * kc * C::ROWB, trq[mbd]), bp[kc],
-                                                                accv[mbd], 0, 0, 0);
-      }
-      // dV^T += dO^T P  or  dK^T += Q^T dS
-      const uint8_t* ab = WANT_DK ? qb : ob;
+      // dV^T += dO^T P, then dK^T += Q^T dS (dO^T, Q^T through transposing reads)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int mbd = 0; mbd < C::MBD; ++mbd)
-          acc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ab + 16 * kc * C::ROWB, trq[mbd]), bf[kc],
-                                                             acc[mbd], 0, 0, 0);
+          accv[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ob + 16 * kc * C::ROWB, trq[mbd]), bp[kc],
+                                                              accv[mbd], 0, 0, 0);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int mbd = 0; mbd < C::MBD; ++mbd)
+          acck[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qb + 16 * kc * C::ROWB, trq[mbd]), bs[kc],
+                                                              acck[mbd], 0, 0, 0);
     };
 
     auto tile = [&](auto stage_tag, int t) {
@@ -478,9 +463,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     }
     __builtin_amdgcn_s_waitcnt(0);  // every load has landed before the work-group ends (no tile: V rows)
     if (key_ok) {
-      if (WANT_DK) store_rowT<D>(p.dk + head_kv + (size_t)kj * D, acc, p.scale, h);
-      else store_rowT<D>(p.dv + head_kv + (size_t)kj * D, acc, 1.f, h);
-      if constexpr (BOTH) store_rowT<D>(p.dv + head_kv + (size_t)kj * D, accv, 1.f, h);
+      store_rowT<D>(p.dk + head_kv + (size_t)kj * D, acck, p.scale, h);
+      store_rowT<D>(p.dv + head_kv + (size_t)kj * D, accv, 1.f, h);
     }
   }
 }
@@ -517,16 +501,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(p.total_q), dim3(C::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (D == 64) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kGradKV>), dim3(p.total_k), dim3(C::NT), 0, s, p);
-    return hipGetLastError();
-  } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kGradV>), dim3(p.total_k), dim3(C::NT), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kGradK>), dim3(p.total_k), dim3(C::NT), 0, s, p);
-    return hipGetLastError();
-  }
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.total_k), dim3(C::NT), 0, s, p);
+  return hipGetLastError();
 }
 
 int64_t bwd_bf16_grid(int B, int H, int Nq, int Nkv) {
