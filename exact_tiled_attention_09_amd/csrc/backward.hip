@@ -14,10 +14,10 @@
 //    with a lane pair per query).  It also computes D from dO and O and stores it for the next kernel.
 //    Per 64-key tile: S^T = K Q^T and dP^T = V dO^T (K, V fragments from LDS), dS^T in registers,
 //    dQ^T += K^T dS^T (K^T through ds_read_b64_tr_b16 of the same K tile).
-//  * bwd_dkdv_kernel: one work-group per (b, h, 128 keys), the same layout with the roles of queries and
-//    keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query block of the 64-query tiles
-//    streamed through LDS: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T
-//    through transposing reads), both gradients in one pass.
+//  * bwd_dkdv_kernel: one work-group per (b, h, 256 keys at d = 128, 128 at d = 64), the same layout
+//    with the roles of queries and keys exchanged (S = Q K^T with a lane pair per key).  Per 32-query
+//    block of the 64-query tiles streamed through LDS: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and
+//    dK^T += Q^T dS (dO^T, Q^T through transposing reads), both gradients in one pass.
 // Tiles read both row-wise (ds_read_b128) and transposed (ds_read_b64_tr_b16) use a swizzle that keeps
 // both access patterns on distinct banks.
 #include "common.h"
@@ -38,7 +38,7 @@ struct BwdParams {
   uint16_t* __restrict__ dk;
   uint16_t* __restrict__ dv;
   int Nq, Nkv, off;
-  int n_qt, n_kt;            // 128-query / 128-key blocks per (b, h)
+  int n_qt, n_kt;            // 128-query blocks (dQ kernel) and key blocks of the dK/dV kernel per (b, h)
   int total_q, total_k;      // work-groups of the two kernels
   int pair_q, pair_k;        // causal: one work-group runs blocks j and n-1-j (equal work per group)
   float c;                   // scale * log2(e) (any sign)
@@ -267,23 +267,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------------------------------------- dK, dV
 
-// One pass forms both gradients from one S and dP per 32x32 key-query block (D/4 MFMAs; two separate
-// dV and dK passes would need 5 D/16 and stream Q, dO twice).  It holds both D x 32 accumulators: at
-// d = 128 the wave's V fragments live in registers next to its K fragments (V rows in LDS would leave
-// one work-group per CU), and the compiler spills a few of those fragments to scratch, reloaded once per
-// block; that still ran 5% faster than the two passes at B1 H32 N8192.  At d = 64 the block's V rows sit
-// in LDS and everything fits at three waves per SIMD.
+// One pass forms both gradients from one S and dP per 32x32 key-query block (D/4 MFMAs; separate dV
+// and dK passes would need 5 D/16 and stream Q, dO twice), holding both D x 32 accumulators and the
+// wave's K fragments in registers and the work-group's V rows in LDS.  At d = 128 the work-group has 8
+// waves (256 keys): the V rows (64 KB) and the Q / dO stages (64 KB) fit one work-group per CU, which
+// still runs two waves per SIMD, and each streamed Q / dO tile serves twice as many keys.  (With 4 waves
+// and V in registers instead, to keep two work-groups per CU, the compiler spilled 24-45 VGPRs and the
+// backward ran 11-13% slower.)  At d = 64, 4 waves and 49 KB of LDS run three waves per SIMD.
+template <int D>
+struct DkdvShape {  // work-group shape of bwd_dkdv_kernel: waves (32 keys each), threads, groups per CU
+  static constexpr int NW = D == 128 ? 8 : 4, NT = 64 * NW, BR = 32 * NW, OCC = D == 128 ? 1 : 2;
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(DkdvShape<D>::NT, DkdvShape<D>::OCC) void bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  constexpr bool VREG = D == 128;  // V fragments of the wave's keys in registers instead of LDS
+  using K = DkdvShape<D>;
   // 64 queries per streamed tile: two 32-query blocks per barrier
   constexpr int BQT = 64, NSB = BQT / 32;
-  constexpr int TQT = BQT * C::ROWB, LPT = TQT / (C::NT * 16);
+  constexpr int TQT = BQT * C::ROWB, LPT = TQT / (K::NT * 16);
+  static_assert(TQT % (K::NT * 16) == 0, "tile loads must divide evenly");
   __shared__ __attribute__((aligned(16))) uint8_t lq0[TQT], ldo0[TQT], lq1[TQT], ldo1[TQT];
   __shared__ __attribute__((aligned(16))) float ll0[BQT], ld0[BQT], ll1[BQT], ld1[BQT];
-  // V of the work-group's 128 keys (B operand of dP = dO V^T) when it is not held in registers
-  __shared__ __attribute__((aligned(16))) uint8_t lvk[VREG ? 16 : C::BR * C::ROWB];
+  // V rows of the work-group's keys (B operand of dP = dO V^T)
+  __shared__ __attribute__((aligned(16))) uint8_t lvk[K::BR * C::ROWB];
   auto qbuf = [&](int st) -> uint8_t* { return st == 0 ? lq0 : lq1; };
   auto obuf = [&](int st) -> uint8_t* { return st == 0 ? ldo0 : ldo1; };
   auto lbuf = [&](int st) -> float* { return st == 0 ? ll0 : ll1; };
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   for (int pass = 0; pass < n_pass; ++pass) {
     const int kt = pass == 0 ? kt_hi : kt_lo;
     if (pass > 0) __syncthreads();  // every wave is done with the LDS stages and V rows before refilling
-    const int k0 = kt * C::BR;
+    const int k0 = kt * K::BR;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));  // lane offsets are recomputed per pass, not held across both
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -310,21 +317,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     const int kw0 = k0 + 32 * w, kj = kw0 + l32;
     const bool key_ok = kj < p.Nkv;
 
-    // K^T and (d = 128) V^T fragments of this lane's key: B operands of S = Q K^T and dP = dO V^T
-    bf16x8 kf[C::KS], vf[VREG ? C::KS : 1];
+    // K^T fragments (B operand of S = Q K^T) of this lane's key
+    bf16x8 kf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 a = {0u, 0u, 0u, 0u}, b = a;
-      if (key_ok) {
-        a = load16(p.k + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
-        if (VREG) b = load16(p.v + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
-      }
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (key_ok) a = load16(p.k + head_kv + (size_t)kj * D + ks * 16 + 8 * h);
       kf[ks] = __builtin_bit_cast(bf16x8, a);
-      if constexpr (VREG) vf[ks] = __builtin_bit_cast(bf16x8, b);
     }
-    if constexpr (!VREG) {  // the block's V rows into LDS (rows past N_kv read zeros); visible after the first barrier
+    {  // the block's V rows into LDS (rows past N_kv read zeros); visible after the first barrier
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_kv + (size_t)k0 * D, (p.Nkv - k0) * C::ROWB);
-      constexpr int LPV = C::BR * C::ROWB / (C::NT * 16);
+      constexpr int LPV = K::BR * C::ROWB / (K::NT * 16);
 #pragma unroll
       for (int i = 0; i < LPV; ++i) {
         const int r = C::RPL * (w * LPV + i) + lane / C::CH, pc = lane % C::CH;
@@ -387,9 +390,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + row_off[ks]);
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
         const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ob + row_off[ks]);
-        bf16x8 vb;
-        if constexpr (VREG) vb = vf[ks];
-        else vb = *reinterpret_cast<const bf16x8*>(vrow + row_off[ks]);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vrow + row_off[ks]);
         dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dP, 0, 0, 0);
       }
       if (first) next();
@@ -489,7 +490,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   p.Nkv = a.Nkv;
   p.off = a.Nkv - a.Nq;
   p.n_qt = (a.Nq + C::BR - 1) / C::BR;
-  p.n_kt = (a.Nkv + C::BR - 1) / C::BR;
+  p.n_kt = (a.Nkv + DkdvShape<D>::BR - 1) / DkdvShape<D>::BR;
   // pair causal blocks when a grid spans at least two work-groups per compute unit (below that every block
   // runs at once and pairing would only lengthen the longest chain)
   p.pair_q = CAUSAL && p.n_qt >= 2 && (int64_t)a.B * a.H * p.n_qt >= 2 * kNumCu;
@@ -501,7 +502,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(p.total_q), dim3(C::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.total_k), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.total_k), dim3(DkdvShape<D>::NT), 0, s, p);
   return hipGetLastError();
 }
 

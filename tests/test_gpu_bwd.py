@@ -76,12 +76,13 @@ def test_bwd_parity(case):
 
 
 # Causal grids of at least two work-groups per compute unit pair blocks j and n-1-j in one work-group, in
-# both kernels (query blocks for dQ, key blocks for dK / dV).
+# both kernels (query blocks of 128 for dQ; key blocks of 256 at d = 128, 128 at d = 64 for dK / dV).
 PAIRED = [
     # B, H, Nq, Nkv, d
     (1, 74, 1100, 1100, 64),    # 9 blocks per head each way: four pairs and a lone middle block; ragged
-    (2, 36, 1000, 1500, 128),   # 8 query blocks, 12 key blocks; queries at the end of a longer cache
+    (2, 36, 1000, 1500, 128),   # 8 query blocks (paired), 6 key blocks (not); queries at the end of a longer cache
     (1, 256, 200, 200, 64),     # exactly 512 work-groups per kernel before pairing
+    (2, 64, 600, 1100, 128),    # d = 128: 5 key blocks of 256 and 5 query blocks of 128 per head, both paired
 ]
 
 
