@@ -206,13 +206,13 @@ def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int, decode_inpu
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
     t = time_events(lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream), stream, steps, warmup)
-    S = 2
+    S = fa.fa_fwd_split_num_splits(w.B, w.H, w.Nq, w.Nkv, w.d)
     ws = torch.empty(fa.fa_fwd_split_workspace_bytes(w.B, w.H, w.Nq, w.d, S), dtype=torch.uint8, device=dev)
     ts = time_events(lambda: fa.fa_fwd_split(q, k, v, o, lse, w.scale, True, S, ws, stream), stream, steps, warmup)
     out["chunked_prefill"] = {"workload": "causal (bottom-right) bf16 B1 H32 N_q1000 N_kv8192 d128",
                               "value": round(w.flops / (ts * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                               "frac_of_peak": round(w.flops / (ts * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                              "entry_point": f"fa_fwd_split, {S} splits + combine", "avg_ms": round(ts, 4),
+                              "entry_point": f"fa_fwd_split, {S} splits (fa_fwd_split_num_splits) + combine", "avg_ms": round(ts, 4),
                               "fa_fwd_single_pass_tflops": round(w.flops / (t * 1e-3) / 1e12, 2)}
     del q, k, v, o, lse, ws
     # grouped key/value decode: 32 query heads over 8 key/value heads, 8192 cached keys

@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_combine.argtypes = [vp, sz, vp, vp, i, i, i, i, vp, i]
     L.fa_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
     L.fa_fwd_split_workspace_bytes.restype = sz
+    L.fa_fwd_split_num_splits.argtypes = [i, i, i, i, i]
+    L.fa_fwd_split_num_splits.restype = i
     L.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp, i]
     L.fa_decode_gqa_num_splits.argtypes = [i, i, i, i, i, i]
     L.fa_decode_gqa_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -187,6 +189,10 @@ def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None):
 
 def fa_fwd_split_workspace_bytes(B: int, H: int, N_q: int, d: int, num_splits: int) -> int:
     return lib().fa_fwd_split_workspace_bytes(B, H, N_q, d, num_splits)
+
+
+def fa_fwd_split_num_splits(B: int, H: int, N_q: int, N_kv: int, d: int) -> int:
+    return lib().fa_fwd_split_num_splits(B, H, N_q, N_kv, d)
 
 
 def fa_fwd_split(q, k, v, o, lse, scale: float, causal: bool, num_splits: int, workspace, stream=None):

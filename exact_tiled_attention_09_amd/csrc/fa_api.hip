@@ -9,6 +9,7 @@
 
 #include <climits>
 
+#include "common.h"
 #include "fa.h"
 #include "kernels.h"
 
@@ -250,6 +251,20 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
   st = fa_decode_split(q, k, v, B, H, N_kv, d, scale, S, workspace, workspace_bytes, stream, dtype);
   if (st != FA_OK) return st;
   return fa_decode_combine(workspace, workspace_bytes, o, lse, B, H, d, S, stream, dtype);
+}
+
+int fa_fwd_split_num_splits(int B, int H, int N_q, int N_kv, int d) {
+  if (B < 1 || H < 1 || N_q < 1 || N_kv < 1 || (d != 64 && d != 128)) return 0;
+  // The split work-groups are bound by matrix-core work, not by bytes in flight: one round of the two
+  // that are resident per compute unit is enough (on a 1000-query chunk against 8192 keys, 2 splits and
+  // 4 splits each won on some GPUs by up to 7%; 3 and 8 lost 10-20% to uneven rounds and the fixed
+  // costs of short splits); no split is made shorter than 512 keys.
+  const int64_t units = (int64_t)B * H * ((N_q + 127) / 128);
+  int64_t s = (2 * fa::kNumCu + units - 1) / units;
+  const int64_t max_by_len = (N_kv + 511) / 512;
+  if (s > max_by_len) s = max_by_len;
+  if (s < 1) s = 1;
+  return (int)s;
 }
 
 size_t fa_fwd_split_workspace_bytes(int B, int H, int N_q, int d, int num_splits) {

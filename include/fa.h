@@ -139,6 +139,11 @@ fa_status fa_decode_combine(const void* workspace, size_t workspace_bytes, void*
  * it" ("Flash Attention Explained: Same Maths, Far Less Memory").
  */
 size_t fa_fwd_split_workspace_bytes(int B, int H, int N_q, int d, int num_splits);
+/* A split count for fa_fwd_split: enough work-groups for two per compute unit
+ * (B*H*ceil(N_q/128)*S ~ 512 on the 256-CU part), no split shorter than 512 keys,
+ * at least 1.  0 for sizes fa_fwd_split rejects (B, H, N_q, N_kv < 1; d not 64 or 128).
+ * Host-only arithmetic, no GPU call. */
+int fa_fwd_split_num_splits(int B, int H, int N_q, int N_kv, int d);
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
                        int N_kv, int d, float scale, int causal, int num_splits, void* workspace,
                        size_t workspace_bytes, void* stream, fa_dtype dtype);

@@ -114,6 +114,13 @@ def test_decode_workspace_arithmetic(L):
     assert fa.fa_decode_num_splits(64, 32, 8192, 128, 0) >= 1
     assert fa.fa_decode_num_splits(1, 1, 10, 64, 0) == 1
     assert fa.fa_decode_num_splits(4, 4, 1000, 64, 3) == 3
+    # split counts for fa_fwd_split: ~512 work-groups, splits of at least 512 keys
+    assert fa.fa_fwd_split_num_splits(1, 32, 1000, 8192, 128) == 2     # 256 query tiles of a chunk
+    assert fa.fa_fwd_split_num_splits(1, 32, 8192, 8192, 128) == 1     # 2048 query tiles already
+    assert fa.fa_fwd_split_num_splits(1, 1, 128, 100000, 64) == 196    # capped by 512-key splits
+    assert fa.fa_fwd_split_num_splits(1, 1, 1, 300, 128) == 1
+    assert fa.fa_fwd_split_num_splits(1, 1, 1, 300, 96) == 0           # unsupported d
+    assert fa.fa_fwd_split_num_splits(0, 1, 1, 300, 64) == 0
 
 
 def dec(L, q=P(0), k=P(1), v=P(2), o=P(3), lse=P(4), B=2, H=2, Nkv=64, d=128, scale=0.1, S=4, ws=P(6),
