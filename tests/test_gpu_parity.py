@@ -151,6 +151,12 @@ EDGE = [
     (1, 2, 200, 200, 128, "bf16", False, 2.0),    # very peaked rows
     (1, 1, 333, 333, 64, "f32", False, 0.0),
     (3, 1, 64, 640, 128, "bf16", False, None),
+    # fp32 grids of at least one work-group per compute unit keep one wave per 32 rows over the whole row;
+    # smaller ones split each row's keys over the waves of a work-group and merge their partials
+    (2, 128, 128, 128, 64, "f32", True, None),    # 256 work-groups: whole-row waves
+    (2, 128, 100, 300, 128, "f32", False, None),  # 256 work-groups: whole-row waves, ragged
+    (1, 3, 40, 70, 64, "f32", True, None),        # key split: 3 tiles for 8 waves, bottom-right causal
+    (1, 1, 33, 33, 128, "f32", True, 0.0),        # key split, uniform weights
 ]
 
 
