@@ -10,6 +10,8 @@
 // a K row (and of its Q row) per 16-byte access and feeds them to 4 consecutive MFMAs.  For
 // O^T = V^T P^T the probability is the lane's own score register and V is read one float per lane
 // from a row-major LDS copy (padded rows against bank conflicts between the two lane halves).
+// Grids with fewer work-groups than compute units use prefill_f32_ks_kernel instead, which splits each
+// row's keys over the waves of a work-group and merges their partials (below).
 #include "common.h"
 #include "kernels.h"
 
