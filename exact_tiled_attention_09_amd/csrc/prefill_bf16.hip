@@ -14,9 +14,10 @@
 // weights that entered the value product (so a dominant weight cancels exactly), the LSE by the fp32
 // sum.  The score tile lives only in registers.
 //
-// gfx950 mapping: one work-group of 4 waves per (batch*head, 128-query tile), 32 query rows per wave,
-// two work-groups per CU (two waves per SIMD: one wave's softmax runs while the other's MFMAs run;
-// s_setprio favours the wave that is in an MFMA phase).
+// gfx950 mapping: 32 query rows per wave, two waves per SIMD (one wave's softmax runs while the other's
+// MFMAs run; s_setprio favours the wave that is in an MFMA phase): 4 waves per (batch*head, 128-query
+// tile) and two work-groups per CU, or, for large d = 128 grids without splits, 8 waves per 256-query
+// tile and one work-group per CU.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS = A operand, Q^T in VGPRs = B operand): in
 //    the 32x32 result a lane holds one query and 16 keys; lanes l and l^32 together hold the row, so
 //    row max / row sum are in-lane reductions plus one v_permlane32_swap.
@@ -73,23 +74,17 @@ struct PrefillParams {
   int pair;  // causal, unsplit: work-group j runs query tile n_qt-1-j, then tile j (set by the launcher)
 };
 
-#ifndef FA_NW
-#define FA_NW 4
-#endif
 #ifndef FA_BC
 #define FA_BC 64
-#endif
-#ifndef FA_OCC
-#define FA_OCC 2
 #endif
 constexpr float kBig = 0x1p64f;  // weights above this trigger a move of the reference maximum
 // instruction classes of __builtin_amdgcn_sched_group_barrier, and the K fragment read-ahead
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 constexpr int kKDepth = 4;
 
-template <int D>
+template <int D, int NWAVES = 4>
 struct Cfg {
-  static constexpr int NW = FA_NW;         // waves per work-group
+  static constexpr int NW = NWAVES;        // waves per work-group
   static constexpr int NT = NW * 64;       // threads
   static constexpr int BR = NW * 32;       // query rows per work-group (32 per wave)
   static constexpr int BC = FA_BC;         // keys per tile
@@ -121,8 +116,9 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
 // NT: K and V are read by exactly one work-group (one query tile per head, as in decode), so their loads
 // use the non-temporal policy (measured +8% on grouped-head decode) instead of staying in the caches for
 // the other query tiles of the head.
-template <int D, bool CAUSAL, bool SPLIT, bool PAGED = false, bool NT = false>
-__global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(PrefillParams p) {
+// NW: waves per work-group, 4 (two work-groups per CU) or 8 (one per CU; used where it measured faster)
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED = false, bool NT = false, int NW = 4>
+__global__ __launch_bounds__(NW * 64, (NW == 8 ? 1 : 2)) void prefill_bf16_kernel(PrefillParams p) {
   static_assert(!PAGED || (SPLIT && !CAUSAL), "the paged cache is read by the unmasked split mode only");
   auto load16_lds = [](__amdgpu_buffer_rsrc_t r, int voff, void* lds_block) {
     if constexpr (NT)
@@ -130,7 +126,7 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
     else
       load_lds16(r, voff, lds_block);
   };
-  using C = Cfg<D>;
+  using C = Cfg<D, NW>;
   // One LDS array per stage and operand: the compiler can then tell that the direct loads into one
   // stage do not alias the fragment reads of the other, and does not wait for those loads before them.
   __shared__ __attribute__((aligned(16))) uint8_t lds_k0[C::TILEB], lds_v0[C::TILEB], lds_k1[C::TILEB], lds_v1[C::TILEB];
@@ -501,13 +497,13 @@ __global__ __launch_bounds__(FA_NW * 64, FA_OCC) void prefill_bf16_kernel(Prefil
 // ---------------------------------------------------------------------------------------------- launch
 
 int64_t prefill_bf16_grid(int B, int H, int Nq, int d, int splits) {
-  const int br = d == 128 ? Cfg<128>::BR : Cfg<64>::BR;
+  const int br = 128;  // the smallest query tile of any launch (an upper bound on the grid)
   return (int64_t)B * H * ((Nq + br - 1) / br) * (splits > 0 ? splits : 1);
 }
 
-template <int D, bool CAUSAL, bool SPLIT, bool PAGED = false, bool NT = false>
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED = false, bool NT = false, int NW = 4>
 static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
-  using C = Cfg<D>;
+  using C = Cfg<D, NW>;
   PrefillParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -537,7 +533,7 @@ static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   // every tile runs at once and pairing would only lengthen the longest chain)
   p.pair = CAUSAL && !SPLIT && p.n_qt >= 2 && (int64_t)a.B * a.H * p.n_qt >= 2 * kNumCu;
   if (p.pair) p.total = a.B * a.H * ((p.n_qt + 1) / 2);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, SPLIT, PAGED, NT>), dim3(p.total), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, SPLIT, PAGED, NT, NW>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -562,6 +558,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     if (a.d == 128) return a.causal ? launch_d<128, true, true>(a, s) : launch_d<128, false, true>(a, s);
     return a.causal ? launch_d<64, true, true>(a, s) : launch_d<64, false, true>(a, s);
   }
+  // d = 128 with at least one 8-wave work-group (256 query rows) per CU: 8 waves, which share each K / V
+  // tile between twice the rows (A/B: +0.5-1.1% at B1 H32 N8192, +2.7% at B1 H8 N32768); smaller grids
+  // (-18% for 1000 queries x 32 heads, half the CUs idle) and d = 64 (-3.5%) keep 4 waves
+  if (a.d == 128 && (int64_t)a.B * a.H * ((a.Nq + 255) / 256) >= kNumCu)
+    return a.causal ? launch_d<128, true, false, false, false, 8>(a, s) : launch_d<128, false, false, false, false, 8>(a, s);
   if (a.d == 128) return a.causal ? launch_d<128, true, false>(a, s) : launch_d<128, false, false>(a, s);
   return a.causal ? launch_d<64, true, false>(a, s) : launch_d<64, false, false>(a, s);
 }

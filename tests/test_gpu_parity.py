@@ -170,12 +170,14 @@ def test_edge_shapes(case):
     check(w, O, L, Oref, Lref)
 
 
-# Causal grids of at least two work-groups per compute unit (B*H*ceil(N_q/128) >= 512) run query tiles in
-# pairs (tile n-1-j, then tile j, in one work-group); every element against the oracle.
+# Causal grids of at least two work-groups per compute unit run query tiles in pairs (tile n-1-j, then tile
+# j, in one work-group); every element against the oracle.  Query tiles are 128 rows (4 waves), or 256
+# rows (8 waves, one work-group per CU) at d = 128 when B*H*ceil(N_q/256) >= 256.
 PAIRED = [
     # B, H, Nq, Nkv, d
+    (1, 128, 1100, 1100, 128),  # 8 waves: 5 tiles of 256 per head, two pairs and a lone middle; ragged
     (1, 74, 1100, 1100, 64),    # 9 tiles per head: four pairs and a lone middle tile; ragged last tile
-    (2, 36, 1000, 1500, 128),   # 8 tiles per head, queries at the end of a longer cache
+    (2, 36, 1000, 1500, 128),   # 8 waves, 4 unpaired tiles of 256, queries at the end of a longer cache
     (1, 256, 200, 200, 64),     # exactly 512 work-groups before pairing: tile 1 then tile 0
     (1, 255, 200, 200, 128),    # 510: just below the threshold, unpaired
 ]
