@@ -5,7 +5,6 @@ from .attention import (  # noqa: F401
     attention_ref,
     combine_ref,
     decode_ref,
-    default_scale,
     gqa_decode_ref,
     merge_partials,
     paged_decode_ref,

@@ -51,7 +51,6 @@ compared with):
 """
 from __future__ import annotations
 
-import math
 
 import numpy as np
 
@@ -318,7 +317,3 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool):
             dk[b, h] = scale * (dS.T @ q[b, h])
     return dq, dk, dv
 
-
-def default_scale(d: int) -> float:
-    """1/sqrt(d_k), the scale of the attention equation."""
-    return 1.0 / math.sqrt(d)
