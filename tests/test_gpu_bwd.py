@@ -1,11 +1,21 @@
 """GPU parity of the backward pass (fa_bwd) against the fp64 gradient oracle.
 
 The forward output o and lse come from fa_fwd (as in training); dO is a seeded N(0,1) bf16 tensor.
-Tolerance (no figure on the pages; derived from the arithmetic): each gradient is a sum of products of
-bf16 operands (P and dS rounded to bf16, 2^-9 relative each) accumulated in fp32, then rounded to bf16
-(2^-9 relative); D uses the bf16-rounded forward output.  The bound applied is
-max|g_gpu - g_ref| <= 1.5e-2 * max|g_ref| per tensor, plus a relative Frobenius error <= 6e-3 (observed:
-at most 5.4e-3 and 2.9e-3, i.e. about twice the 2^-9 rounding of the bf16 output).
+
+Tolerance, derived before looking at any result (the pages give no figure).  The kernels compute
+P = exp(s - LSE) in fp32 from fp32 scores, round P to bf16 for dV = P^T dO, form dS = P * (dP - D) in fp32
+with D = rowsum(dO * O) taken from the bf16 forward output, round dS to bf16 for dQ = scale dS K and
+dK = scale dS^T Q, accumulate every product in fp32 and round each gradient to bf16.  With the bf16 unit
+roundoff u = 2^-8, first-order error analysis of those steps bounds every element by
+    |d dV| <= u (|P|^T |dO|) + u |dV|
+    |d dQ| <= scale (u |dS| |K| + (|P| * dD) |K|) + u |dQ|
+    |d dK| <= scale (u |dS|^T |Q| + (|P| * dD)^T |Q|) + u |dK|
+where dD = 2u rowsum(|dO| * (|P| |V|)) bounds the error of D through the forward output (its own bf16
+weights and its bf16 rounding).  fp32 accumulation (n 2^-24 relative, n <= 8192) and the fp32 scores,
+exponentials and LSE add terms orders of magnitude smaller, which the factor 2 of the bar covers together
+with the second-order terms: the test requires |g - g_ref| <= 2 x bound for every element of dQ, dK, dV.
+rounding_bound() computes the bound from the fp64 inputs; it is a tolerance, not a value compared with.
+Each case also prints max|g - g_ref| / max|g_ref| and the relative Frobenius error (observations only).
 """
 import numpy as np
 import pytest
@@ -16,7 +26,34 @@ from tests.gpu_util import to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
-TOL_MAX, TOL_FRO = 1.5e-2, 6e-3
+U = 2.0 ** -8  # bf16 unit roundoff
+
+
+def rounding_bound(q, k, v, do, scale, causal):
+    """Elementwise first-order bounds (dq, dk, dv) of the errors the kernels' bf16 roundings can cause,
+    computed from the fp64 inputs [B, H, N, d] one (b, h) slice at a time."""
+    bq, bk, bv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    n_q, n_kv = q.shape[2], k.shape[2]
+    allowed = np.arange(n_kv)[None, :] <= np.arange(n_q)[:, None] + (n_kv - n_q) if causal else None
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            Q, K, V, dO = q[b, h], k[b, h], v[b, h], do[b, h]
+            s = scale * Q @ K.T
+            if causal:
+                s = np.where(allowed, s, -np.inf)
+            p = np.exp(s - s.max(-1, keepdims=True))
+            p /= p.sum(-1, keepdims=True)
+            o = p @ V
+            dp = dO @ V.T
+            dd = (dO * o).sum(-1, keepdims=True)
+            ds = p * (dp - dd)
+            dq, dk, dv = scale * ds @ K, scale * ds.T @ Q, p.T @ dO
+            e_d = 2 * U * (np.abs(dO) * (p @ np.abs(V))).sum(-1, keepdims=True)  # error of D
+            pe = p * e_d                                                          # its effect on dS
+            bv[b, h] = U * (p.T @ np.abs(dO)) + U * np.abs(dv)
+            bq[b, h] = abs(scale) * (U * (np.abs(ds) @ np.abs(K)) + pe @ np.abs(K)) + U * np.abs(dq)
+            bk[b, h] = abs(scale) * (U * (np.abs(ds).T @ np.abs(Q)) + pe.T @ np.abs(Q)) + U * np.abs(dk)
+    return bq, bk, bv
 
 
 def fa():
@@ -35,17 +72,29 @@ def run_case(B, H, Nq, Nkv, d, causal, scale, seed, dist=None):
     dq, dk, dv = fa().attention_backward(q, k, v, o, lse, do, w.scale, causal)
     torch.cuda.synchronize()
     ref = attention_bwd_ref(f64["q"], f64["k"], f64["v"], f64["do"], w.scale, causal)
+    bounds = rounding_bound(f64["q"], f64["k"], f64["v"], f64["do"], w.scale, causal)
     out = {}
-    for name, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+    for name, got, r, bd in (("dq", dq, ref[0], bounds[0]), ("dk", dk, ref[1], bounds[1]),
+                             ("dv", dv, ref[2], bounds[2])):
         g = to_host64(got)
         assert np.all(np.isfinite(g)), name
         scale_ref = max(np.abs(r).max(), 1e-30)
         e_max = np.abs(g - r).max() / scale_ref
         e_fro = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
-        print(f"  {name}: max|err|/max|ref| = {e_max:.3e}  frobenius rel = {e_fro:.3e}  (max|ref| {scale_ref:.3e})",
-              flush=True)
-        out[name] = (e_max, e_fro, g, r)
+        ratio = within_bound(g, r, bd)
+        print(f"  {name}: max|err|/(2 x bound) = {ratio:.3f}  [max|err|/max|ref| = {e_max:.3e}  frobenius rel = "
+              f"{e_fro:.3e}  max|ref| {scale_ref:.3e}]", flush=True)
+        out[name] = (ratio, g, r)
     return out
+
+
+def within_bound(g, r, bound):
+    """max over elements of |g - r| / (2 x bound); elements whose bound is exactly 0 must match exactly."""
+    err = np.abs(g - r)
+    zero = bound == 0
+    if np.any(err[zero] != 0):
+        return float("inf")
+    return float((err[~zero] / (2 * bound[~zero])).max()) if np.any(~zero) else 0.0
 
 
 CASES = [
@@ -67,12 +116,8 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}q{}kv{}d{}c{}s{}".format(*c))
 def test_bwd_parity(case):
     out = run_case(*case, seed=200 + CASES.index(case))
-    for name, (e_max, e_fro, g, r) in out.items():
-        if np.abs(r).max() == 0.0:
-            assert np.abs(g).max() == 0.0, name
-            continue
-        assert e_max <= TOL_MAX, f"{name}: {e_max}"
-        assert e_fro <= TOL_FRO, f"{name}: {e_fro}"
+    for name, (ratio, g, r) in out.items():
+        assert ratio <= 1.0, f"{name}: error / (2 x rounding bound) = {ratio}"
 
 
 # Causal grids of at least two work-groups per compute unit pair blocks j and n-1-j in one work-group, in
@@ -90,56 +135,22 @@ PAIRED = [
 def test_bwd_paired_blocks(case):
     B, H, Nq, Nkv, d = case
     out = run_case(B, H, Nq, Nkv, d, True, None, seed=450 + PAIRED.index(case))
-    for name, (e_max, e_fro, g, r) in out.items():
-        assert e_max <= TOL_MAX, f"{name}: {e_max}"
-        assert e_fro <= TOL_FRO, f"{name}: {e_fro}"
-
-
-def dq_rounding_bound(q, k, v, do, scale, causal):
-    """First-order bound on |dQ_gpu - dQ_exact| from the bf16 roundings the backward takes by design
-    (unit roundoff u = 2^-8): dS rounded for the dQ product, D = rowsum(dO * O) from the bf16 forward
-    output, and the bf16 output itself.  Computed from the fp64 inputs; it is a tolerance, not a value
-    to compare against."""
-    u = 2.0 ** -8
-    s = scale * q @ np.swapaxes(k, -1, -2)
-    if causal:
-        n_q, n_kv = s.shape[-2:]
-        allowed = np.arange(n_kv)[None, :] <= np.arange(n_q)[:, None] + (n_kv - n_q)
-        s = np.where(allowed, s, -np.inf)
-    p = np.exp(s - s.max(-1, keepdims=True))
-    p /= p.sum(-1, keepdims=True)
-    o = p @ v
-    dp = do @ np.swapaxes(v, -1, -2)
-    dd = (do * o).sum(-1, keepdims=True)
-    ds = p * (dp - dd)
-    dq = scale * ds @ k
-    b_ds = u * (np.abs(ds) @ np.abs(k))
-    b_d = u * (np.abs(do) * np.abs(o)).sum(-1, keepdims=True) * (p @ np.abs(k))
-    return scale * (b_ds + b_d) + u * np.abs(dq)
+    for name, (ratio, g, r) in out.items():
+        assert ratio <= 1.0, f"{name}: error / (2 x rounding bound) = {ratio}"
 
 
 @pytest.mark.parametrize("dist", [{"q": "pos", "k": "ramp", "v": "normal"}, {"q": "normal16", "k": "normal",
                                                                               "v": "normal"}],
                          ids=["rising_scores", "peaked_rows"])
 def test_bwd_stress_inputs(dist):
-    """Scores that rise along the keys (LSE up to ~118) and very peaked rows.  dK and dV keep the usual
-    bar.  For dQ = scale * sum_j dS_ij k_j the rising keys share a large common part that cancels in the
-    sum (sum_j dS_ij = 0), so the bf16 roundings of dS and of O (through D) are amplified: dQ is held to
-    twice their first-order bound instead."""
-    import torch
+    """Scores that rise along the keys (LSE up to ~118) and very peaked rows.  For dQ = scale sum_j dS_ij k_j
+    the rising keys share a large common part that cancels in the sum (sum_j dS_ij = 0), so the bf16
+    roundings of dS and of O (through D) are amplified far beyond u |dQ|: the elementwise bound accounts
+    for exactly that through |dS| |K| and (|P| dD) |K|."""
     B, H, N, d, seed = 1, 2, 600, 128, 250
-    w = syn.custom(B, H, N, N, d, "bf16", True, None, seed=seed, dist=dist)
     out = run_case(B, H, N, N, d, True, None, seed=seed, dist=dist)
-    for name in ("dk", "dv"):
-        e_max, e_fro, _, _ = out[name]
-        assert e_max <= TOL_MAX, f"{name}: {e_max}"
-        assert e_fro <= TOL_FRO, f"{name}: {e_fro}"
-    _, _, g, r = out["dq"]
-    f64 = {t: syn.as_f64(syn.make_tensor(w, t), "bf16") for t in ("q", "k", "v", "do")}
-    bound = dq_rounding_bound(f64["q"], f64["k"], f64["v"], f64["do"], w.scale, True)
-    ratio = (np.abs(g - r) / (2 * bound + 1e-30)).max()
-    print(f"  dq: max |err| / (2 x rounding bound) = {ratio:.3f}", flush=True)
-    assert ratio <= 1.0
+    for name, (ratio, g, r) in out.items():
+        assert ratio <= 1.0, f"{name}: error / (2 x rounding bound) = {ratio}"
 
 
 def test_bwd_deterministic():
@@ -167,11 +178,13 @@ def test_bwd_full_causal_prefill_one_head_sampled():
     dq, dk, dv = fa().attention_backward(q, k, v, o, lse, do, w.scale, True)
     torch.cuda.synchronize()
     ref = attention_bwd_ref(f64["q"], f64["k"], f64["v"], f64["do"], w.scale, True)
+    bounds = rounding_bound(f64["q"], f64["k"], f64["v"], f64["do"], w.scale, True)
     rows = np.unique(np.concatenate([np.arange(0, 8192, 97), [1, 127, 128, 4095, 8190, 8191]]))
-    for name, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+    for name, got, r, bd in (("dq", dq, ref[0], bounds[0]), ("dk", dk, ref[1], bounds[1]),
+                             ("dv", dv, ref[2], bounds[2])):
         g = to_host64(got)
         assert np.all(np.isfinite(g)), name
-        e = np.abs(g[0, 0, rows] - r[0, 0, rows]).max() / np.abs(r).max()
-        print(f"  {name}: max|err|/max|ref| on {rows.size} rows = {e:.3e}", flush=True)
-        assert e <= TOL_MAX, f"{name}: {e}"
+        ratio = within_bound(g[0, 0, rows], r[0, 0, rows], bd[0, 0, rows])
+        print(f"  {name}: max|err|/(2 x bound) on {rows.size} rows = {ratio:.3f}", flush=True)
+        assert ratio <= 1.0, f"{name}: {ratio}"
 
