@@ -22,7 +22,17 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_DEVICE = range(5)
 FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1
 
+FA_PLAN_FWD, FA_PLAN_FWD_SPLIT, FA_PLAN_DECODE, FA_PLAN_BWD_DQ, FA_PLAN_BWD_DKDV = range(5)
+KERNEL_NAMES = {1: "bf16_4wave", 2: "bf16_8wave", 3: "bf16_split", 4: "f32_rows", 5: "f32_keysplit",
+                6: "decode_split", 7: "bwd_dq", 8: "bwd_dkdv"}
+
 _lib = None
+
+
+class PlanInfo(ctypes.Structure):
+    """fa_plan_info of include/fa.h."""
+    _fields_ = [("kernel", ctypes.c_int), ("waves_per_group", ctypes.c_int), ("rows_per_group", ctypes.c_int),
+                ("paired", ctypes.c_int), ("groups", ctypes.c_longlong), ("num_splits", ctypes.c_int)]
 
 
 class FaError(RuntimeError):
@@ -67,6 +77,14 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
     L.fa_bwd_workspace_bytes.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp, i]
+    L.fa_plan.argtypes = [i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(PlanInfo)]
+    L.fa_plan.restype = ctypes.c_int
+    L.fa_device_num_cu.argtypes = []
+    L.fa_device_num_cu.restype = ctypes.c_int
+    L.fa_probe_read_bandwidth.argtypes = [vp, sz, vp, sz, i, vp]
+    L.fa_probe_read_bandwidth.restype = ctypes.c_int
+    L.fa_probe_clock.argtypes = [vp, sz, i, i, vp]
+    L.fa_probe_clock.restype = ctypes.c_int
     L.fa_status_str.argtypes = [i]
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_last_error.argtypes = []
@@ -116,6 +134,8 @@ def _dtype_code(t) -> int:
 
 
 def _check_tensor(name, t, shape, dtype):
+    """Every tensor handed to the library: a contiguous device tensor of the expected shape and dtype (the C
+    layer sees only a pointer, so a strided view or a host tensor would be read as something else)."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
@@ -124,6 +144,35 @@ def _check_tensor(name, t, shape, dtype):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _check_workspace(t):
+    """A workspace: a contiguous device tensor of bytes (uint8); returns its size in bytes."""
+    import torch
+    if not t.is_cuda:
+        raise ValueError("workspace must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if t.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a uint8 (byte) tensor, got {t.dtype}")
+    return t.numel()
+
+
+def plan(op: int, B: int, H: int, N_q: int, N_kv: int, d: int, causal: bool = True, dtype: int = FA_DTYPE_BF16,
+         num_splits: int = 0, num_cu: int = 0) -> dict:
+    """fa_plan: the launch decisions of an entry point for these sizes on a device with num_cu compute units
+    (0 = the current device).  Host arithmetic only when num_cu > 0."""
+    info = PlanInfo()
+    st = lib().fa_plan(op, B, H, N_q, N_kv, d, int(bool(causal)), dtype, num_splits, num_cu, ctypes.byref(info))
+    _check(st, "fa_plan")
+    return {"kernel": KERNEL_NAMES.get(info.kernel, info.kernel), "waves_per_group": info.waves_per_group,
+            "rows_per_group": info.rows_per_group, "paired": bool(info.paired), "groups": info.groups,
+            "num_splits": info.num_splits}
+
+
+def device_num_cu() -> int:
+    """Compute units of the current device (0 when none can be queried)."""
+    return lib().fa_device_num_cu()
 
 
 # ----------------------------------------------------------------------------- C entry points, torch arguments
@@ -157,33 +206,38 @@ def fa_decode(q, k, v, o, lse, scale: float, num_splits: int, workspace, stream=
     workspace a byte (uint8) device tensor of at least fa_decode_workspace_bytes()."""
     import torch
     B, H, Nkv, d = k.shape
+    _check_tensor("k", k, (B, H, Nkv, d), k.dtype)
     _check_tensor("q", q, (B, H, d), k.dtype)
     _check_tensor("v", v, (B, H, Nkv, d), k.dtype)
     _check_tensor("o", o, (B, H, d), k.dtype)
     if lse is not None:
         _check_tensor("lse", lse, (B, H), torch.float32)
+    nws = _check_workspace(workspace)
     st = lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nkv, d, float(scale), int(num_splits),
-                         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
-                         _dtype_code(k))
+                         _ptr(workspace), nws, _stream(stream), _dtype_code(k))
     _check(st, "fa_decode")
 
 
 def fa_decode_split(q, k, v, scale: float, num_splits: int, workspace, stream=None):
     B, H, Nkv, d = k.shape
+    _check_tensor("k", k, (B, H, Nkv, d), k.dtype)
     _check_tensor("q", q, (B, H, d), k.dtype)
     _check_tensor("v", v, (B, H, Nkv, d), k.dtype)
+    nws = _check_workspace(workspace)
     st = lib().fa_decode_split(_ptr(q), _ptr(k), _ptr(v), B, H, Nkv, d, float(scale), int(num_splits), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream), _dtype_code(k))
+                               nws, _stream(stream), _dtype_code(k))
     _check(st, "fa_decode_split")
 
 
 def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None):
     import torch
     B, H, d = o.shape
+    _check_tensor("o", o, (B, H, d), o.dtype)
     if lse is not None:
         _check_tensor("lse", lse, (B, H), torch.float32)
-    st = lib().fa_decode_combine(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(o), _ptr(lse),
-                                 B, H, d, int(num_splits), _stream(stream), _dtype_code(o))
+    nws = _check_workspace(workspace)
+    st = lib().fa_decode_combine(_ptr(workspace), nws, _ptr(o), _ptr(lse), B, H, d, int(num_splits), _stream(stream),
+                                 _dtype_code(o))
     _check(st, "fa_decode_combine")
 
 
@@ -201,14 +255,16 @@ def fa_fwd_split(q, k, v, o, lse, scale: float, causal: bool, num_splits: int, w
     import torch
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
+    _check_tensor("q", q, (B, H, Nq, d), q.dtype)
     _check_tensor("k", k, (B, H, Nkv, d), q.dtype)
     _check_tensor("v", v, (B, H, Nkv, d), q.dtype)
     _check_tensor("o", o, (B, H, Nq, d), q.dtype)
     if lse is not None:
         _check_tensor("lse", lse, (B, H, Nq), torch.float32)
+    nws = _check_workspace(workspace)
     st = lib().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nkv, d, float(scale),
-                            int(bool(causal)), int(num_splits), _ptr(workspace),
-                            workspace.numel() * workspace.element_size(), _stream(stream), _dtype_code(q))
+                            int(bool(causal)), int(num_splits), _ptr(workspace), nws, _stream(stream),
+                            _dtype_code(q))
     _check(st, "fa_fwd_split")
 
 
@@ -226,14 +282,15 @@ def fa_decode_gqa(q, k, v, o, lse, scale: float, num_splits: int, workspace, str
     import torch
     B, H, d = q.shape
     Hkv, Nkv = k.shape[1], k.shape[2]
+    _check_tensor("k", k, (B, Hkv, Nkv, d), k.dtype)
     _check_tensor("q", q, (B, H, d), k.dtype)
     _check_tensor("v", v, (B, Hkv, Nkv, d), k.dtype)
     _check_tensor("o", o, (B, H, d), k.dtype)
     if lse is not None:
         _check_tensor("lse", lse, (B, H), torch.float32)
+    nws = _check_workspace(workspace)
     st = lib().fa_decode_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nkv, d, float(scale),
-                             int(num_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                             _stream(stream), _dtype_code(k))
+                             int(num_splits), _ptr(workspace), nws, _stream(stream), _dtype_code(k))
     _check(st, "fa_decode_gqa")
 
 
@@ -262,10 +319,10 @@ def fa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, o, lse, scale: f
     _check_tensor("o", o, (B, H, d), k_pages.dtype)
     if lse is not None:
         _check_tensor("lse", lse, (B, H), torch.float32)
+    nws = _check_workspace(workspace)
     st = lib().fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(o),
                                _ptr(lse), B, H, Hkv, n_pages, P, max_blocks, d, float(scale), int(num_splits),
-                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
-                               _dtype_code(k_pages))
+                               _ptr(workspace), nws, _stream(stream), _dtype_code(k_pages))
     _check(st, "fa_decode_paged")
 
 
@@ -279,14 +336,39 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool, worksp
     import torch
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
-    for name, t, n in (("o", o, Nq), ("dout", dout, Nq), ("dq", dq, Nq), ("k", k, Nkv), ("v", v, Nkv),
-                       ("dk", dk, Nkv), ("dv", dv, Nkv)):
+    for name, t, n in (("q", q, Nq), ("o", o, Nq), ("dout", dout, Nq), ("dq", dq, Nq), ("k", k, Nkv),
+                       ("v", v, Nkv), ("dk", dk, Nkv), ("dv", dv, Nkv)):
         _check_tensor(name, t, (B, H, n, d), q.dtype)
     _check_tensor("lse", lse, (B, H, Nq), torch.float32)
+    nws = _check_workspace(workspace)
     st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                      B, H, Nq, Nkv, d, float(scale), int(bool(causal)), _ptr(workspace),
-                      workspace.numel() * workspace.element_size(), _stream(stream), _dtype_code(q))
+                      B, H, Nq, Nkv, d, float(scale), int(bool(causal)), _ptr(workspace), nws, _stream(stream),
+                      _dtype_code(q))
     _check(st, "fa_bwd")
+
+
+# ----------------------------------------------------------------------------- measurement probes (fa_probe.h)
+
+def probe_read_bandwidth(buf, sink, groups: int, stream=None):
+    """fa_probe_read_bandwidth: one non-temporal streaming read of the byte tensor buf; sink is a device
+    tensor of at least groups * 512 int32 words."""
+    _check_workspace(buf)
+    if not sink.is_cuda or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous device tensor")
+    st = lib().fa_probe_read_bandwidth(_ptr(buf), buf.numel(), _ptr(sink), sink.numel() * sink.element_size(),
+                                       int(groups), _stream(stream))
+    if st != 0:
+        raise FaError(FA_ERR_INVALID_ARG if st == 1 else FA_ERR_DEVICE, "fa_probe_read_bandwidth", f"status {st}")
+
+
+def probe_clock(out, groups: int, iters: int, stream=None):
+    """fa_probe_clock: out is an int64 device tensor of at least 5 * groups words."""
+    import torch
+    if not out.is_cuda or not out.is_contiguous() or out.dtype != torch.int64:
+        raise ValueError("out must be a contiguous int64 device tensor")
+    st = lib().fa_probe_clock(_ptr(out), out.numel(), int(groups), int(iters), _stream(stream))
+    if st != 0:
+        raise FaError(FA_ERR_INVALID_ARG if st == 1 else FA_ERR_DEVICE, "fa_probe_clock", f"status {st}")
 
 
 # ----------------------------------------------------------------------------- allocation helpers

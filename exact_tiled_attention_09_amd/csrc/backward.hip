@@ -493,8 +493,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   p.n_kt = (a.Nkv + DkdvShape<D>::BR - 1) / DkdvShape<D>::BR;
   // pair causal blocks when a grid spans at least two work-groups per compute unit (below that every block
   // runs at once and pairing would only lengthen the longest chain)
-  p.pair_q = CAUSAL && p.n_qt >= 2 && (int64_t)a.B * a.H * p.n_qt >= 2 * kNumCu;
-  p.pair_k = CAUSAL && p.n_kt >= 2 && (int64_t)a.B * a.H * p.n_kt >= 2 * kNumCu;
+  p.pair_q = plan_bwd_dq(a.B, a.H, a.Nq, D, CAUSAL, a.num_cu).paired;
+  p.pair_k = plan_bwd_dkdv(a.B, a.H, a.Nkv, D, CAUSAL, a.num_cu).paired;
   p.total_q = a.B * a.H * (p.pair_q ? (p.n_qt + 1) / 2 : p.n_qt);
   p.total_k = a.B * a.H * (p.pair_k ? (p.n_kt + 1) / 2 : p.n_kt);
   p.c = a.scale * kLog2e;
@@ -504,6 +504,28 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.total_k), dim3(DkdvShape<D>::NT), 0, s, p);
   return hipGetLastError();
+}
+
+LaunchPlan plan_bwd_dq(int B, int H, int Nq, int d, bool causal, int num_cu) {
+  LaunchPlan pl;
+  pl.kernel = kKernelBwdDq;
+  pl.waves = d == 128 ? BwdCfg<128>::NW : BwdCfg<64>::NW;
+  pl.rows = d == 128 ? BwdCfg<128>::BR : BwdCfg<64>::BR;
+  const int n = (Nq + pl.rows - 1) / pl.rows;
+  pl.paired = causal && n >= 2 && (int64_t)B * H * n >= 2 * (int64_t)num_cu;
+  pl.groups = (int64_t)B * H * (pl.paired ? (n + 1) / 2 : n);
+  return pl;
+}
+
+LaunchPlan plan_bwd_dkdv(int B, int H, int Nkv, int d, bool causal, int num_cu) {
+  LaunchPlan pl;
+  pl.kernel = kKernelBwdDkdv;
+  pl.waves = d == 128 ? DkdvShape<128>::NT / 64 : DkdvShape<64>::NT / 64;
+  pl.rows = d == 128 ? DkdvShape<128>::BR : DkdvShape<64>::BR;
+  const int n = (Nkv + pl.rows - 1) / pl.rows;
+  pl.paired = causal && n >= 2 && (int64_t)B * H * n >= 2 * (int64_t)num_cu;
+  pl.groups = (int64_t)B * H * (pl.paired ? (n + 1) / 2 : n);
+  return pl;
 }
 
 int64_t bwd_bf16_grid(int B, int H, int Nq, int Nkv) {

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <climits>
 
 #include "common.h"
@@ -57,6 +58,15 @@ fa_status device_status(hipError_t e, const char* what) {
   return fail(FA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// An error left pending on this thread by earlier work is reported as such (and nothing is launched):
+// clearing it silently would hide the caller's failure, and launching on top of it would report it as ours.
+fa_status take_pending(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return ok();
+  return fail(FA_ERR_DEVICE, "%s: an error from earlier work was pending on this thread: %s (nothing was launched)",
+              what, hipGetErrorString(e));
+}
+
 fa_status check_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q, int N_kv,
                     int d, float scale, int causal, fa_dtype dtype, size_t* esz) {
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
@@ -92,10 +102,11 @@ fa_status check_fwd(const void* q, const void* k, const void* v, void* o, float*
   return FA_OK;
 }
 
-int auto_splits(int B, int H, int N_kv) {
-  // Enough work-groups to cover 256 CUs several times, without splits shorter than 256 keys.
+int auto_splits(int B, int H, int N_kv, int num_cu) {
+  // Enough work-groups to cover the CUs eight times (decode is bound by the bytes in flight), without
+  // splits shorter than 256 keys.
   const int64_t bh = (int64_t)B * H;
-  int64_t s = (2048 + bh - 1) / bh;
+  int64_t s = (8 * (int64_t)num_cu + bh - 1) / bh;
   const int64_t max_by_len = (N_kv + 255) / 256;
   if (s > max_by_len) s = max_by_len;
   if (s < 1) s = 1;
@@ -108,7 +119,7 @@ fa_status check_decode_sizes(int B, int H, int N_kv, int d, int num_splits, int*
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head size d=%d is not built (supported: 64, 128)", d);
   if (num_splits < 0 || num_splits > N_kv)
     return fail(FA_ERR_INVALID_ARG, "num_splits must be in [0, N_kv] (got %d)", num_splits);
-  *S = num_splits == 0 ? auto_splits(B, H, N_kv) : num_splits;
+  *S = num_splits == 0 ? auto_splits(B, H, N_kv, fa::planning_cu_count()) : num_splits;
   int64_t el;
   if (!mul_ok(el, {B, H, N_kv, d}) || el > kMaxElems) return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
   int64_t g;
@@ -127,6 +138,51 @@ fa_status check_workspace(const void* ws, size_t have, size_t need) {
 
 }  // namespace
 
+namespace fa {
+
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();  // no usable device: nothing can be launched on this thread anyway
+    return 0;
+  }
+  const int have = cache[dev].load(std::memory_order_relaxed);
+  if (have > 0) return have;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int planning_cu_count() {
+  const int n = device_cu_count();
+  return n > 0 ? n : kDefaultNumCu;
+}
+
+}  // namespace fa
+
+namespace {
+
+int fwd_split_auto(int B, int H, int N_q, int N_kv, int num_cu) {
+  // The split work-groups are bound by matrix-core work, not by bytes in flight: one round of the two
+  // that are resident per compute unit is enough (on a 1000-query chunk against 8192 keys, 2 splits and
+  // 4 splits each won on some GPUs by up to 7%; 3 and 8 lost 10-20% to uneven rounds and the fixed
+  // costs of short splits); no split is made shorter than 512 keys.
+  const int64_t units = (int64_t)B * H * ((N_q + 127) / 128);
+  int64_t s = (2 * (int64_t)num_cu + units - 1) / units;
+  const int64_t max_by_len = (N_kv + 511) / 512;
+  if (s > max_by_len) s = max_by_len;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+}  // namespace
+
 extern "C" {
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q, int N_kv,
@@ -135,7 +191,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   const fa_status st = check_fwd(q, k, v, o, lse, B, H, N_q, N_kv, d, scale, causal, dtype, &esz);
   if (st != FA_OK) return st;
   fa::PrefillArgs a{q, k, v, o, lse, B, H, N_q, N_kv, d, scale, causal != 0};
-  (void)hipGetLastError();
+  a.num_cu = fa::planning_cu_count();
+  const fa_status pend = take_pending("fa_fwd");
+  if (pend != FA_OK) return pend;
   const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_prefill_bf16(a, (hipStream_t)stream)
                                               : fa::launch_prefill_f32(a, (hipStream_t)stream);
   return device_status(e, "fa_fwd launch");
@@ -183,7 +241,8 @@ fa_status fa_decode_split(const void* q, const void* k, const void* v, int B, in
     return fail(FA_ERR_INVALID_ARG, "workspace overlaps an input");
   float* ws_o = static_cast<float*>(workspace);
   fa::DecodeArgs a{q, k, v, B, H, N_kv, d, scale, S, ws_o, ws_o + (size_t)B * H * S * d};
-  (void)hipGetLastError();
+  const fa_status pend = take_pending("fa_decode_split");
+  if (pend != FA_OK) return pend;
   return device_status(fa::launch_decode_split_bf16(a, (hipStream_t)stream), "fa_decode split launch");
 }
 
@@ -211,7 +270,8 @@ fa_status fa_decode_combine(const void* workspace, size_t workspace_bytes, void*
   }
   const float* ws_o = static_cast<const float*>(workspace);
   fa::CombineArgs a{ws_o, ws_o + (size_t)B * H * num_splits * d, o, lse, B, H, d, num_splits};
-  (void)hipGetLastError();
+  const fa_status pend = take_pending("fa_decode_combine");
+  if (pend != FA_OK) return pend;
   return device_status(fa::launch_decode_combine_bf16(a, (hipStream_t)stream), "fa_decode combine launch");
 }
 
@@ -255,16 +315,7 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
 
 int fa_fwd_split_num_splits(int B, int H, int N_q, int N_kv, int d) {
   if (B < 1 || H < 1 || N_q < 1 || N_kv < 1 || (d != 64 && d != 128)) return 0;
-  // The split work-groups are bound by matrix-core work, not by bytes in flight: one round of the two
-  // that are resident per compute unit is enough (on a 1000-query chunk against 8192 keys, 2 splits and
-  // 4 splits each won on some GPUs by up to 7%; 3 and 8 lost 10-20% to uneven rounds and the fixed
-  // costs of short splits); no split is made shorter than 512 keys.
-  const int64_t units = (int64_t)B * H * ((N_q + 127) / 128);
-  int64_t s = (2 * fa::kNumCu + units - 1) / units;
-  const int64_t max_by_len = (N_kv + 511) / 512;
-  if (s > max_by_len) s = max_by_len;
-  if (s < 1) s = 1;
-  return (int)s;
+  return fwd_split_auto(B, H, N_q, N_kv, fa::planning_cu_count());
 }
 
 size_t fa_fwd_split_workspace_bytes(int B, int H, int N_q, int d, int num_splits) {
@@ -299,7 +350,9 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = ws_o + (size_t)B * H * N_q * num_splits * d;
   fa::PrefillArgs a{q, k, v, o, lse, B, H, N_q, N_kv, d, scale, causal != 0, num_splits, ws_o, ws_lse};
-  (void)hipGetLastError();
+  a.num_cu = fa::planning_cu_count();
+  const fa_status pend = take_pending("fa_fwd_split");
+  if (pend != FA_OK) return pend;
   hipError_t e = fa::launch_prefill_bf16(a, (hipStream_t)stream);
   if (e != hipSuccess) return device_status(e, "fa_fwd_split launch");
   fa::CombineArgs cmb{ws_o, ws_lse, o, lse, B * H * N_q, 1, d, num_splits};
@@ -403,6 +456,8 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
     return fail(FA_ERR_INVALID_ARG, "workspace overlaps another tensor");
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = ws_o + (size_t)B * H * S * d;
+  const fa_status pend = take_pending("fa_decode_paged");
+  if (pend != FA_OK) return pend;
   if (mfma_path) {
     // the G query heads of a key/value head are the query rows of one split forward over its pages
     fa::PrefillArgs a{q, k_pages, v_pages, nullptr, nullptr, B, H_kv, G, (int)max_len, d, scale, false};
@@ -469,8 +524,57 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   }
   fa::BwdArgs a{q, k, v, o, dout, lse, static_cast<float*>(workspace), dq, dk, dv, B, H, N_q, N_kv, d, scale,
                 causal != 0};
-  (void)hipGetLastError();
+  a.num_cu = fa::planning_cu_count();
+  const fa_status pend = take_pending("fa_bwd");
+  if (pend != FA_OK) return pend;
   return device_status(fa::launch_bwd_bf16(a, (hipStream_t)stream), "fa_bwd launch");
+}
+
+int fa_device_num_cu(void) { return fa::device_cu_count(); }
+
+fa_status fa_plan(fa_plan_op op, int B, int H, int N_q, int N_kv, int d, int causal, fa_dtype dtype, int num_splits,
+                  int num_cu, fa_plan_info* out) {
+  if (!out) return fail(FA_ERR_INVALID_ARG, "out must be non-NULL");
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 1 || H < 1 || N_q < 1 || N_kv < 1 || num_cu < 0 || num_splits < 0)
+    return fail(FA_ERR_INVALID_ARG, "B, H, N_q, N_kv must be >= 1 and num_cu, num_splits >= 0");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head size d=%d is not built (supported: 64, 128)", d);
+  if (op != FA_PLAN_FWD && dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "only fa_fwd is built for fp32");
+  const int cu = num_cu > 0 ? num_cu : fa::planning_cu_count();
+  fa::LaunchPlan pl;
+  int S = 0;
+  switch (op) {
+    case FA_PLAN_FWD:
+      pl = dtype == FA_DTYPE_BF16 ? fa::plan_prefill_bf16(B, H, N_q, d, causal != 0, 0, cu)
+                                  : fa::plan_prefill_f32(B, H, N_q, d, cu);
+      break;
+    case FA_PLAN_FWD_SPLIT:
+      S = num_splits > 0 ? num_splits : fwd_split_auto(B, H, N_q, N_kv, cu);
+      pl = fa::plan_prefill_bf16(B, H, N_q, d, causal != 0, S, cu);
+      break;
+    case FA_PLAN_DECODE:
+      S = num_splits > 0 ? num_splits : auto_splits(B, H, N_kv, cu);
+      pl.kernel = fa::kKernelDecodeSplit;
+      pl.waves = 8;
+      pl.rows = 1;
+      pl.groups = (int64_t)B * H * S;
+      break;
+    case FA_PLAN_BWD_DQ:
+      pl = fa::plan_bwd_dq(B, H, N_q, d, causal != 0, cu);
+      break;
+    case FA_PLAN_BWD_DKDV:
+      pl = fa::plan_bwd_dkdv(B, H, N_kv, d, causal != 0, cu);
+      break;
+    default:
+      return fail(FA_ERR_INVALID_ARG, "unknown plan op %d", (int)op);
+  }
+  out->kernel = pl.kernel;
+  out->waves_per_group = pl.waves;
+  out->rows_per_group = pl.rows;
+  out->paired = pl.paired ? 1 : 0;
+  out->groups = pl.groups;
+  out->num_splits = S;
+  return FA_OK;
 }
 
 const char* fa_status_str(fa_status s) {

@@ -7,6 +7,36 @@
 
 namespace fa {
 
+// Compute units of the full MI355X / MI350X (8 XCDs x 32): the launch heuristics' assumption when the
+// device cannot be asked (host-only sizing calls on a machine without a visible device).
+constexpr int kDefaultNumCu = 256;
+
+// Compute units of the current device, read once per device and cached; 0 if no device can be queried.
+int device_cu_count();
+// device_cu_count(), or kDefaultNumCu when it is 0.
+int planning_cu_count();
+
+// Kernel identifiers reported by fa_plan (values of fa_kernel_id in fa.h).
+enum KernelId : int {
+  kKernelBf16FourWave = 1,
+  kKernelBf16EightWave = 2,
+  kKernelBf16Split = 3,
+  kKernelF32Rows = 4,
+  kKernelF32KeySplit = 5,
+  kKernelDecodeSplit = 6,
+  kKernelBwdDq = 7,
+  kKernelBwdDkdv = 8,
+};
+
+// A launch decision: which kernel, its work-group shape and grid.
+struct LaunchPlan {
+  int kernel = 0;
+  int waves = 0;          // waves per work-group
+  int rows = 0;           // query rows (keys for the dK/dV kernel) per work-group
+  bool paired = false;    // causal tiles n-1-j and j in one work-group
+  int64_t groups = 0;     // work-groups launched
+};
+
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -25,6 +55,7 @@ struct PrefillArgs {
   const int* block_table = nullptr;  // [B, max_blocks]
   const int* seq_lens = nullptr;     // [B]
   int num_pages = 0, page_size = 0, max_blocks = 0;
+  int num_cu = kDefaultNumCu;  // compute units of the device the launch goes to (sizes pairing and wave counts)
 };
 
 struct DecodeArgs {
@@ -73,6 +104,7 @@ struct BwdArgs {
   int B, H, Nq, Nkv, d;
   float scale;
   bool causal;
+  int num_cu = kDefaultNumCu;
 };
 
 // Each launcher assumes validated arguments and returns the launch status.
@@ -85,6 +117,12 @@ hipError_t launch_decode_split_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_combine_bf16(const CombineArgs& a, hipStream_t s);
 hipError_t launch_decode_paged_bf16(const PagedDecodeArgs& a, hipStream_t s);  // G = H / H_kv in {1, 2, 4, 8}
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+
+// The launch decisions of the launchers above, for a device with num_cu compute units.
+LaunchPlan plan_prefill_bf16(int B, int H, int Nq, int d, bool causal, int splits, int num_cu);
+LaunchPlan plan_prefill_f32(int B, int H, int Nq, int d, int num_cu);
+LaunchPlan plan_bwd_dq(int B, int H, int Nq, int d, bool causal, int num_cu);
+LaunchPlan plan_bwd_dkdv(int B, int H, int Nkv, int d, bool causal, int num_cu);
 
 // Grid-size helpers shared with argument validation.
 int64_t prefill_bf16_grid(int B, int H, int Nq, int d, int splits = 0);

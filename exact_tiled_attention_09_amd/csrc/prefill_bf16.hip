@@ -531,10 +531,25 @@ static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   p.lg_page = lg;
   // pair causal query tiles when the grid spans at least two work-groups per compute unit (below that
   // every tile runs at once and pairing would only lengthen the longest chain)
-  p.pair = CAUSAL && !SPLIT && p.n_qt >= 2 && (int64_t)a.B * a.H * p.n_qt >= 2 * kNumCu;
+  p.pair = CAUSAL && !SPLIT && p.n_qt >= 2 && (int64_t)a.B * a.H * p.n_qt >= 2 * (int64_t)a.num_cu;
   if (p.pair) p.total = a.B * a.H * ((p.n_qt + 1) / 2);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, SPLIT, PAGED, NT, NW>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
+}
+
+LaunchPlan plan_prefill_bf16(int B, int H, int Nq, int d, bool causal, int splits, int num_cu) {
+  LaunchPlan pl;
+  // d = 128 with at least one 8-wave work-group (256 query rows) per CU: 8 waves, which share each K / V
+  // tile between twice the rows (A/B: +0.5-1.1% at B1 H32 N8192, +2.7% at B1 H8 N32768); smaller grids
+  // (-18% for 1000 queries x 32 heads, half the CUs idle) and d = 64 (-3.5%) keep 4 waves
+  const bool eight = splits == 0 && d == 128 && (int64_t)B * H * ((Nq + 255) / 256) >= num_cu;
+  pl.kernel = splits > 0 ? kKernelBf16Split : (eight ? kKernelBf16EightWave : kKernelBf16FourWave);
+  pl.waves = eight ? 8 : 4;
+  pl.rows = 32 * pl.waves;
+  const int n_qt = (Nq + pl.rows - 1) / pl.rows;
+  pl.paired = causal && splits == 0 && n_qt >= 2 && (int64_t)B * H * n_qt >= 2 * (int64_t)num_cu;
+  pl.groups = (int64_t)B * H * (pl.paired ? (n_qt + 1) / 2 : n_qt) * (splits > 0 ? splits : 1);
+  return pl;
 }
 
 int prefill_split_tiles(int Nkv, int S) {
@@ -558,10 +573,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     if (a.d == 128) return a.causal ? launch_d<128, true, true>(a, s) : launch_d<128, false, true>(a, s);
     return a.causal ? launch_d<64, true, true>(a, s) : launch_d<64, false, true>(a, s);
   }
-  // d = 128 with at least one 8-wave work-group (256 query rows) per CU: 8 waves, which share each K / V
-  // tile between twice the rows (A/B: +0.5-1.1% at B1 H32 N8192, +2.7% at B1 H8 N32768); smaller grids
-  // (-18% for 1000 queries x 32 heads, half the CUs idle) and d = 64 (-3.5%) keep 4 waves
-  if (a.d == 128 && (int64_t)a.B * a.H * ((a.Nq + 255) / 256) >= kNumCu)
+  if (plan_prefill_bf16(a.B, a.H, a.Nq, a.d, a.causal, 0, a.num_cu).waves == 8)
     return a.causal ? launch_d<128, true, false, false, false, 8>(a, s) : launch_d<128, false, false, false, false, 8>(a, s);
   if (a.d == 128) return a.causal ? launch_d<128, true, false>(a, s) : launch_d<128, false, false>(a, s);
   return a.causal ? launch_d<64, true, false>(a, s) : launch_d<64, false, false>(a, s);

@@ -362,7 +362,7 @@ static hipError_t launch_f32_d(const PrefillArgs& a, hipStream_t s) {
   p.total = a.B * a.H * p.n_qt;
   p.c = fabsf(a.scale) * kLog2e;
   p.qxor = a.scale < 0.f ? 0x80000000u : 0u;
-  if (p.total < kNumCu) {  // fewer work-groups than compute units: split each row's keys over the waves
+  if (plan_prefill_f32(a.B, a.H, a.Nq, D, a.num_cu).kernel == kKernelF32KeySplit) {
     constexpr int KW = D == 64 ? 8 : 4;
     p.n_qt = (a.Nq + 31) / 32;
     p.total = a.B * a.H * p.n_qt;
@@ -371,6 +371,24 @@ static hipError_t launch_f32_d(const PrefillArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL((prefill_f32_kernel<D, kNWf, kBCf, CAUSAL>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
+}
+
+LaunchPlan plan_prefill_f32(int B, int H, int Nq, int d, int num_cu) {
+  LaunchPlan pl;
+  const int64_t rows_grid = prefill_f32_grid(B, H, Nq, d);
+  // fewer work-groups than compute units: split each row's keys over the waves of a 32-row work-group
+  if (rows_grid < num_cu) {
+    pl.kernel = kKernelF32KeySplit;
+    pl.waves = d == 64 ? 8 : 4;
+    pl.rows = 32;
+    pl.groups = (int64_t)B * H * ((Nq + 31) / 32);
+  } else {
+    pl.kernel = kKernelF32Rows;
+    pl.waves = kNWf;
+    pl.rows = kNWf * 32;
+    pl.groups = rows_grid;
+  }
+  return pl;
 }
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {

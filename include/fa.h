@@ -29,12 +29,21 @@
  *             device.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *             stream of the current device) and the call returns; outputs are valid
  *             once the caller has synchronised that stream.  Inputs are read-only.
- *  Errors     Every argument is validated on the host before anything is launched;
- *             on a non-OK status nothing was enqueued and the outputs are untouched.
- *             A launch failure returns FA_ERR_DEVICE.  fa_last_error() gives a
- *             thread-local description of the last non-OK status.  No exception or
- *             abort crosses this boundary.
- *  Threads    Re-entrant; the only global state is the thread-local error text.
+ *  Errors     Every argument is validated on the host before anything is launched:
+ *             on FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_WORKSPACE nothing
+ *             was enqueued and the outputs are untouched.  FA_ERR_DEVICE means the
+ *             HIP runtime refused a launch; an entry point that enqueues two kernels
+ *             (fa_decode, fa_fwd_split, fa_decode_gqa, fa_decode_paged, fa_bwd) may
+ *             then have enqueued the first, so its outputs are undefined.  An error
+ *             already pending on the calling thread from earlier work (the HIP
+ *             runtime's last-error state) is reported as FA_ERR_DEVICE before any
+ *             launch instead of being cleared.  fa_last_error() gives a thread-local
+ *             description of the last non-OK status.  No exception or abort crosses
+ *             this boundary.
+ *  Threads    Re-entrant; the global state is the thread-local error text and a
+ *             per-device cache of the compute-unit count, read once on first use
+ *             (launch heuristics such as causal tile pairing, wave counts and the
+ *             automatic split counts are sized by it).
  *  Results    Bitwise deterministic run to run for the same arguments.
  */
 #ifndef FA_H_
@@ -51,7 +60,7 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1, /* NULL/misaligned/overlapping pointer, size < 1, causal with N_q > N_kv, ... */
   FA_ERR_UNSUPPORTED = 2, /* valid request outside the built domain (head size, dtype) */
   FA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than fa_decode_workspace_bytes() */
-  FA_ERR_DEVICE = 4       /* the HIP runtime refused a launch */
+  FA_ERR_DEVICE = 4       /* the HIP runtime refused a launch, or an error from earlier work was pending */
 } fa_status;
 
 typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 } fa_dtype;
@@ -97,7 +106,9 @@ fa_status fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float
  *   float lse_s[B, H, S]         at byte offset B*H*S*d*4
  */
 
-/* The split count fa_decode uses for num_splits == 0 (auto); >= 1. Returns 0 on invalid sizes. */
+/* The split count fa_decode uses for num_splits == 0 (auto): enough (b, h, split)
+ * work-groups for eight per compute unit of the current device, no split shorter than
+ * 256 keys; >= 1.  Returns 0 on invalid sizes. */
 int fa_decode_num_splits(int B, int H, int N_kv, int d, int num_splits);
 
 /* Workspace bytes fa_decode needs for these sizes (num_splits 0 = auto). Returns 0 on invalid sizes. */
@@ -139,10 +150,10 @@ fa_status fa_decode_combine(const void* workspace, size_t workspace_bytes, void*
  * it" ("Flash Attention Explained: Same Maths, Far Less Memory").
  */
 size_t fa_fwd_split_workspace_bytes(int B, int H, int N_q, int d, int num_splits);
-/* A split count for fa_fwd_split: enough work-groups for two per compute unit
- * (B*H*ceil(N_q/128)*S ~ 512 on the 256-CU part), no split shorter than 512 keys,
- * at least 1.  0 for sizes fa_fwd_split rejects (B, H, N_q, N_kv < 1; d not 64 or 128).
- * Host-only arithmetic, no GPU call. */
+/* A split count for fa_fwd_split: enough work-groups for two per compute unit of the
+ * current device (B*H*ceil(N_q/128)*S ~ 2 * CUs), no split shorter than 512 keys, at
+ * least 1.  0 for sizes fa_fwd_split rejects (B, H, N_q, N_kv < 1; d not 64 or 128).
+ * Host-only apart from the one-time CU-count query. */
 int fa_fwd_split_num_splits(int B, int H, int N_q, int N_kv, int d);
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
                        int N_kv, int d, float scale, int causal, int num_splits, void* workspace,
@@ -236,7 +247,59 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* dq, void* dk, void* dv, int B, int H, int N_q, int N_kv, int d, float scale, int causal,
                  void* workspace, size_t workspace_bytes, void* stream, fa_dtype dtype);
 
-/* Human-readable name of a status code (static storage). */
+/*
+ * Launch plans: which kernel, work-group shape and grid an entry point would use
+ * for these sizes on a device with num_cu compute units (0 = the current device;
+ * 256, the full MI355X, when none is visible).  The heuristics depend on the CU
+ * count only through these decisions, never through the results' meaning.  Host
+ * arithmetic only (no GPU call when num_cu > 0); for tests and tuning.
+ *   op            FA_PLAN_FWD: fa_fwd (dtype bf16 or f32); FA_PLAN_FWD_SPLIT:
+ *                 fa_fwd_split; FA_PLAN_DECODE: the split kernel of fa_decode
+ *                 (N_q ignored); FA_PLAN_BWD_DQ / FA_PLAN_BWD_DKDV: the two
+ *                 kernels of fa_bwd.  Split ops take num_splits (0 = automatic).
+ *   out           filled on FA_OK.
+ * Returns FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED for sizes the entry point rejects
+ * for the same reasons (sizes < 1, d not 64 or 128, fp32 outside fa_fwd).
+ */
+typedef enum {
+  FA_PLAN_FWD = 0,
+  FA_PLAN_FWD_SPLIT = 1,
+  FA_PLAN_DECODE = 2,
+  FA_PLAN_BWD_DQ = 3,
+  FA_PLAN_BWD_DKDV = 4
+} fa_plan_op;
+
+typedef enum {
+  FA_KERNEL_BF16_4WAVE = 1,    /* bf16 forward, 4 waves x 32 query rows, two work-groups per CU */
+  FA_KERNEL_BF16_8WAVE = 2,    /* bf16 forward, 8 waves x 32 query rows, one work-group per CU */
+  FA_KERNEL_BF16_SPLIT = 3,    /* bf16 split-KV forward (partials + combine) */
+  FA_KERNEL_F32_ROWS = 4,      /* fp32 forward, each wave walks its rows' whole key range */
+  FA_KERNEL_F32_KEYSPLIT = 5,  /* fp32 forward, a 32-row work-group's waves split the keys */
+  FA_KERNEL_DECODE_SPLIT = 6,  /* decode: one work-group per (b, h, split) */
+  FA_KERNEL_BWD_DQ = 7,        /* backward, dQ kernel */
+  FA_KERNEL_BWD_DKDV = 8       /* backward, fused dK / dV kernel */
+} fa_kernel_id;
+
+typedef struct {
+  int kernel;           /* fa_kernel_id */
+  int waves_per_group;  /* waves per work-group */
+  int rows_per_group;   /* query rows per work-group (keys for FA_KERNEL_BWD_DKDV, 1 for decode) */
+  int paired;           /* 1: causal tiles n-1-j and j share a work-group (equal work per group) */
+  long long groups;     /* work-groups launched */
+  int num_splits;       /* split count of the split ops, else 0 */
+} fa_plan_info;
+
+fa_status fa_plan(fa_plan_op op, int B, int H, int N_q, int N_kv, int d, int causal, fa_dtype dtype, int num_splits,
+                  int num_cu, fa_plan_info* out);
+
+/* Compute units of the current device (read once per device), 0 when no device can be queried. */
+int fa_device_num_cu(void);
+
+/* Human-readable name of a status code (static storage).  Together with fa_last_error it
+ * serves the rule that an unsupported or invalid request is a visible error, never a
+ * silent fallback to another code path ("Flash Attention Explained: Same Maths, Far Less
+ * Memory", "The takeaway"; "FlashAttention Explained: How AI Models Process Attention
+ * Faster and Use Less Memory", "Best Practices for Using FlashAttention"). */
 const char* fa_status_str(fa_status s);
 
 /* Thread-local text describing the last non-OK status returned on this thread ("" if none). */

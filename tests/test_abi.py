@@ -12,6 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "fa_probe.h")]
 
 fa = pytest.importorskip("exact_tiled_attention_09_amd")
 
@@ -23,10 +24,12 @@ def L():
     return fa.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+def declared_functions(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -208,3 +211,16 @@ def test_paged_workspace_arithmetic(L):
 def test_paged_rejects(L, kw, status):
     assert paged(L, **kw) == status
     assert fa.last_error() != ""
+
+
+def test_probes_reject_bad_arguments(L):
+    sink = ctypes.c_void_p(A * 7)
+    # NULL, misaligned or too small arguments: status 1, nothing launched
+    assert L.fa_probe_read_bandwidth(None, 1 << 20, sink, 1 << 20, 4, None) == 1
+    assert L.fa_probe_read_bandwidth(ctypes.c_void_p(A + 8), 1 << 20, sink, 1 << 20, 4, None) == 1
+    assert L.fa_probe_read_bandwidth(P(0), 8, sink, 1 << 20, 4, None) == 1
+    assert L.fa_probe_read_bandwidth(P(0), 1 << 20, sink, 4 * 512 * 4 - 1, 4, None) == 1
+    assert L.fa_probe_read_bandwidth(P(0), 1 << 20, sink, 1 << 20, 0, None) == 1
+    assert L.fa_probe_clock(None, 100, 4, 10, None) == 1
+    assert L.fa_probe_clock(P(0), 19, 4, 10, None) == 1
+    assert L.fa_probe_clock(P(0), 20, 4, 0, None) == 1
