@@ -9,8 +9,10 @@ A step is one pass over every kernel of the path on its workload, inputs already
 W untimed warm-up steps, then K timed steps between device synchronisations.  Every launch is
 bracketed by HIP events on the stream it runs on, which gives each kernel's average duration over
 the timed region.  value = prefill TFLOP/s (algorithmic flops 4*d per allowed pair / kernel time);
-the decode figures (GB/s of algorithmic bytes) sit in "decode".  The CPU oracle is timed on a
-bounded sample of the prefill workload in the same run ("cpu_baseline").
+the decode figures (GB/s of algorithmic bytes) sit in "decode".  "context" holds the read bandwidth of a
+plain streaming kernel and the shader clock under dense MFMA load, measured in the same run.  The CPU
+oracle is timed on the host cores in the same run ("cpu_baseline": one worker process per core, whole
+heads of the prefill workload, bounded samples of the other four).
 """
 from __future__ import annotations
 
@@ -64,13 +66,16 @@ TRAFFIC_KERNELS = {
                          "exact_tiled_attention_09_amd/csrc/lds_tiles.h"]),
     "decode_split_c5": ("decode", "decode_split_kernel",
                         ["exact_tiled_attention_09_amd/csrc/decode.hip", "exact_tiled_attention_09_amd/csrc/common.h"]),
+    "prefill_bf16_c4": ("prefill_c4", "prefill_bf16_kernel",
+                        ["exact_tiled_attention_09_amd/csrc/prefill_bf16.hip", "exact_tiled_attention_09_amd/csrc/common.h",
+                         "exact_tiled_attention_09_amd/csrc/lds_tiles.h"]),
 }
 
 
 def write_traffic(run_dir: str, copy_bytes: int = 1 << 30):
     """Build profiles/traffic.json from rocprofv3 --pmc runs of this script: <run_dir>/<prefix>.<COUNTER>/
-    holding p_counter_collection.csv for prefix copy (--copy-bytes), prefill (--only prefill) and decode
-    (--only decode), COUNTER in FETCH_SIZE, WRITE_SIZE.  The copy of known size gives the factor that turns
+    holding p_counter_collection.csv for prefix copy (--copy-bytes), prefill (--only prefill), decode
+    (--only decode) and prefill_c4 (--only prefill_c4), COUNTER in FETCH_SIZE, WRITE_SIZE.  The copy of known size gives the factor that turns
     each counter's KiB into bytes."""
     import csv
     import glob
@@ -96,7 +101,8 @@ def write_traffic(run_dir: str, copy_bytes: int = 1 << 30):
                             "note": "device-to-device copy of copy_bytes: bytes = counter KiB * 1024 * factor"}}
     wp, wd = syn.WORKLOADS["c3"], syn.WORKLOADS["c5"]
     alg = {"prefill_bf16_c3": wp.io_bytes,
-           "decode_split_c5": 2 * wd.B * wd.H * wd.Nkv * wd.d * 2 + wd.B * wd.H * wd.d * 2}
+           "decode_split_c5": 2 * wd.B * wd.H * wd.Nkv * wd.d * 2 + wd.B * wd.H * wd.d * 2,
+           "prefill_bf16_c4": syn.WORKLOADS["c4"].io_bytes}
     for name, (prefix, kernel, sources) in TRAFFIC_KERNELS.items():
         fk, n = per_dispatch(prefix, "FETCH_SIZE", kernel)
         wk, _ = per_dispatch(prefix, "WRITE_SIZE", kernel)
@@ -254,78 +260,129 @@ def time_next(fa, syn, upload, dev, stream, steps: int, warmup: int, decode_inpu
     return out
 
 
-def cpu_baseline(target_s: float = 12.0):
-    """Time the fp64 oracle (as it stands) on a bounded sample of the causal prefill workload."""
+def _warm(_):
+    """Worker start-up: imports only (not timed)."""
+    import synthetic  # noqa: F401
+    import oracle  # noqa: F401
+    return os.getpid()
+
+
+def _oracle_head(args):
+    """Worker: the oracle on one whole (b, h) slice of a workload (inputs generated in the worker, not
+    timed).  Returns (seconds, flops)."""
+    cfg, b, h, rows = args
+    from threadpoolctl import threadpool_limits
+
     import synthetic as syn
     from oracle import attention_ref
-    w = syn.WORKLOADS["c3"]
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        pass
-    cores = len(os.sched_getaffinity(0))
-    # whole heads, one after another, until the time budget is used: every row is a full causal row
-    heads, flops, t_total = 0, 0, 0.0
-    rows = np.arange(w.Nq)
-    for h in range(w.H):
-        q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=[(0, h)]), "bf16")[None] for t in "qkv")
+    w = syn.WORKLOADS[cfg]
+    with threadpool_limits(1):
+        q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=[(b, h)], workers=1), w.dtype)[None] for t in "qkv")
         t0 = time.perf_counter()
-        attention_ref(q, k, v, w.scale, True)
-        t_total += time.perf_counter() - t0
-        flops += int(4 * w.d * (rows + 1).sum())
-        heads += 1
-        if t_total >= target_s:
-            break
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads or cores,
-            "kind": "oracle",
-            "sample": f"causal bf16 prefill B1 H32 N8192 d128: {heads} of 32 heads, every row, "
-                      f"{flops / 1e9:.1f} GFLOP in fp64 in {t_total:.1f} s on {cores} host cores",
-            "per_config": cpu_baseline_other_configs()}
-
-
-def cpu_baseline_other_configs(budget_s: float = 1.5):
-    """The oracle's rate on bounded samples of the other four workloads: whole heads (c1, c2), evenly spaced
-    full causal rows of one head (c4), whole decode rows (c5)."""
-    import synthetic as syn
-    from oracle import attention_ref, decode_ref
-    out = {}
-    for cfg in ("c1", "c2"):
-        w = syn.WORKLOADS[cfg]
-        heads, flops, t_total = 0, 0, 0.0
-        pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
-        per_head = w.flops // len(pairs)
-        for b, h in pairs:
-            q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=[(b, h)]), w.dtype)[None] for t in "qkv")
-            t0 = time.perf_counter()
+        if rows is None:
             attention_ref(q, k, v, w.scale, w.causal)
-            t_total += time.perf_counter() - t0
-            flops += per_head
-            heads += 1
-            if t_total >= budget_s:
-                break
-        out[cfg] = {"value": round(flops / t_total / 1e12, 4), "unit": "TFLOP/s", "wall_s": round(t_total, 3),
-                    "sample": f"{w.name}: {heads} of {len(pairs)} heads"}
-    w = syn.WORKLOADS["c4"]
-    q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=[(0, 0)]), "bf16")[None] for t in "qkv")
-    rows = np.linspace(0, w.Nq - 1, 512).astype(np.int64)
-    t0 = time.perf_counter()
-    attention_ref(q, k, v, w.scale, True, rows=rows)
-    t_total = time.perf_counter() - t0
-    flops = int(4 * w.d * (rows + 1).sum())
-    out["c4"] = {"value": round(flops / t_total / 1e12, 4), "unit": "TFLOP/s", "wall_s": round(t_total, 3),
-                 "sample": f"{w.name}: 512 evenly spaced causal rows of head 0"}
+            n = w.flops // (w.B * w.H)
+        else:
+            r = np.asarray(rows)
+            attention_ref(q, k, v, w.scale, w.causal, rows=r)
+            n = int(4 * w.d * (r + 1 + (w.Nkv - w.Nq)).sum()) if w.causal else 4 * w.d * w.Nkv * len(r)
+        return time.perf_counter() - t0, n, os.getpid()
+
+
+def _oracle_decode_rows(args):
+    """Worker: the oracle on whole decode rows (b, h) of the decode workload.  Returns (seconds, bytes)."""
+    pairs, = args
+    from threadpoolctl import threadpool_limits
+
+    import synthetic as syn
+    from oracle import decode_ref
     w = syn.WORKLOADS["c5"]
-    pairs = [(b, h) for b in range(0, w.B, 4) for h in range(0, w.H, 8)][:64]
-    q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=pairs), "bf16")[None] for t in "qkv")
-    t0 = time.perf_counter()
-    decode_ref(q[:, :, 0], k, v, w.scale)
-    t_total = time.perf_counter() - t0
-    by = len(pairs) * (2 * w.Nkv * w.d * 2 + w.d * 2)
-    out["c5"] = {"value": round(by / t_total / 1e9, 3), "unit": "GB/s (bf16 q, K, V bytes)",
-                 "wall_s": round(t_total, 3), "sample": f"{w.name}: {len(pairs)} of {w.B * w.H} (b, h) rows"}
+    with threadpool_limits(1):
+        q, k, v = (syn.as_f64(syn.make_tensor(w, t, bh=pairs, workers=1), "bf16")[None] for t in "qkv")
+        t0 = time.perf_counter()
+        decode_ref(q[:, :, 0], k, v, w.scale)
+        return time.perf_counter() - t0, len(pairs) * (2 * w.Nkv * w.d * 2 + w.d * 2), os.getpid()
+
+
+def cpu_baseline():
+    """The fp64 oracle as it stands, on the host cores: one worker process per core (started fresh, not
+    forked from this GPU process), BLAS held to one thread per worker, each worker taking whole heads.  The
+    headline sample is every head of the causal prefill workload; bounded samples of the other four
+    workloads follow.  Rate = work done / wall time of the pool."""
+    import multiprocessing as mp
+
+    import synthetic as syn
+    cores = len(os.sched_getaffinity(0))
+    ctx = mp.get_context("spawn")
+
+    def run(fn, tasks):
+        """(oracle seconds, results): the largest per-worker sum of timed oracle work, i.e. the wall time of
+        the pool with the input generation (done in the workers, untimed) left out."""
+        with ctx.Pool(cores) as pool:
+            pool.map(_warm, range(cores))  # start-up imports, not timed
+            res = pool.map(fn, tasks, chunksize=1)
+        per_worker = {}
+        for r in res:
+            per_worker[r[2]] = per_worker.get(r[2], 0.0) + r[0]
+        return max(per_worker.values()), res
+
+    w = syn.WORKLOADS["c3"]
+    wall, res = run(_oracle_head, [("c3", 0, h, None) for h in range(w.H)])
+    flops = sum(r[1] for r in res)
+    out = {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "workers": f"{cores} processes (spawned), BLAS threads 1 each, one whole head per task",
+           "sample": f"causal bf16 prefill B1 H32 N8192 d128: all {w.H} heads, every row, {flops / 1e9:.1f} GFLOP "
+                     f"in fp64 in {wall:.2f} s on {cores} host cores (busiest worker's oracle time; "
+                     f"{sum(r[0] for r in res):.1f} s of oracle time over all workers)"}
+    per = {}
+    for cfg in ("c1", "c2"):
+        wc = syn.WORKLOADS[cfg]
+        tasks = [(cfg, b, h, None) for b in range(wc.B) for h in range(wc.H)]
+        wall, res = run(_oracle_head, tasks)
+        per[cfg] = {"value": round(sum(r[1] for r in res) / wall / 1e12, 4), "unit": "TFLOP/s",
+                    "wall_s": round(wall, 3), "sample": f"{wc.name}: all {len(tasks)} heads"}
+    wc = syn.WORKLOADS["c4"]
+    rows = np.linspace(0, wc.Nq - 1, 512).astype(np.int64)
+    tasks = [("c4", 0, h, rows[i::2].tolist()) for h in range(wc.H) for i in range(2)]
+    wall, res = run(_oracle_head, tasks)
+    per["c4"] = {"value": round(sum(r[1] for r in res) / wall / 1e12, 4), "unit": "TFLOP/s", "wall_s": round(wall, 3),
+                 "sample": f"{wc.name}: 512 evenly spaced causal rows of each of the {wc.H} heads"}
+    wc = syn.WORKLOADS["c5"]
+    pairs = [(b, h) for b in range(0, wc.B, 2) for h in range(0, wc.H, 4)]
+    tasks = [(pairs[i::cores],) for i in range(cores) if pairs[i::cores]]
+    wall, res = run(_oracle_decode_rows, tasks)
+    per["c5"] = {"value": round(sum(r[1] for r in res) / wall / 1e9, 3), "unit": "GB/s (bf16 q, K, V bytes)",
+                 "wall_s": round(wall, 3), "sample": f"{wc.name}: {len(pairs)} of {wc.B * wc.H} (b, h) rows"}
+    out["per_config"] = per
     return out
+
+
+def machine_context(fa, dev, stream, read_buf, steps: int = 5):
+    """Measured machine figures beside the kernels' own: the read bandwidth of a plain non-temporal
+    streaming kernel over read_buf (a byte view of a device tensor far larger than the caches) and the
+    shader clock under dense MFMA load (s_memtime against the 100 MHz s_memrealtime)."""
+    import torch
+    n_cu = fa.device_num_cu() or 256
+    groups = 8 * n_cu
+    sink = torch.empty(groups * 512, dtype=torch.int32, device=dev)
+    t = time_events(lambda: fa.probe_read_bandwidth(read_buf, sink, groups, stream), stream, steps, 2)
+    gbs = read_buf.numel() / (t * 1e-3) / 1e9
+    cgroups, iters = 2 * n_cu, 10000
+    out = torch.zeros(5 * cgroups, dtype=torch.int64, device=dev)
+    tc = time_events(lambda: fa.probe_clock(out, cgroups, iters, stream), stream, 3, 1)
+    o = out.view(cgroups, 5).cpu().numpy().astype(np.float64)
+    mhz = 100.0 * (o[:, 2] - o[:, 0]) / np.maximum(o[:, 3] - o[:, 1], 1)
+    assert not o[:, 4].any(), "clock probe accumulators went NaN"
+    mfma_tflops = cgroups * 4 * (-(-iters // 8) * 64) * 32768 / (tc * 1e-3) / 1e12
+    return {"read_stream": {"value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                            "bytes": read_buf.numel(), "avg_ms": round(t, 4),
+                            "kernel": "fa_probe_read_bandwidth: 16-byte non-temporal loads, 4 in flight per "
+                                      f"thread, {groups} groups of 512 taking 32 KB chunks in turn"},
+            "sclk_under_mfma": {"median_mhz": round(float(np.median(mhz)), 1), "min_mhz": round(float(mhz.min()), 1),
+                                "max_mhz": round(float(mhz.max()), 1), "mfma_tflops": round(mfma_tflops, 1),
+                                "kernel": f"fa_probe_clock: {cgroups} groups x 4 waves x {iters * 8} bf16 "
+                                          "32x32x16 MFMAs on changing pseudo-random operands"},
+            "num_cu": n_cu}
 
 
 def main():
@@ -334,9 +391,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "prefill", "decode", "f32", "next"], default="all",
+    ap.add_argument("--only", choices=["all", "step", "prefill", "decode", "f32", "next", "prefill_c2", "prefill_c4",
+                                       "backward"], default="all",
                     help="launch only this part (for profiler runs): 'step' is the timed step without the extra "
-                         "workloads, 'next' only the extra workloads; the JSON line is still printed")
+                         "workloads, 'next' only the extra workloads; 'prefill_c2' / 'prefill_c4' the other two causal "
+                         "bf16 prefill workloads and 'backward' fa_bwd on the headline prefill workload, each "
+                         "--warmup + --steps times (a JSON line with their mean times is printed)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the step, run 5 device-to-device copies of this many bytes (calibrates "
                          "the profiler's HBM byte counters against a copy of known size) and exit")
@@ -374,6 +434,26 @@ def main():
         if dtype == "f32":
             return torch.from_numpy(x).to(dev)
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.only in ("prefill_c2", "prefill_c4", "backward"):  # one workload alone, for profiler runs
+        w = syn.WORKLOADS["c3" if args.only == "backward" else args.only[-2:]]
+        q, k, v = (upload(syn.make_tensor(w, t), "bf16") for t in "qkv")
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream)
+        if args.only == "backward":
+            do = upload(syn.make_tensor(w, "do"), "bf16")
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq), dtype=torch.uint8, device=dev)
+            fn = lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, w.scale, True, ws, stream)  # noqa: E731
+            fl = 2.5 * w.flops
+        else:
+            fn = lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream)  # noqa: E731
+            fl = w.flops
+        t = time_events(fn, stream, args.steps, args.warmup)
+        print(json.dumps({"workload": f"{args.only} {w.name}", "avg_ms": round(t, 4),
+                          "tflops": round(fl / (t * 1e-3) / 1e12, 2)}))
+        return
 
     wp, wd, w1 = syn.WORKLOADS["c3"], syn.WORKLOADS["c5"], syn.WORKLOADS["c1"]
     run_p = args.only in ("all", "step", "prefill")
@@ -507,6 +587,9 @@ def main():
         "wall_s_timed": round(wall, 4),
         "gpu": torch.cuda.get_device_name(0),
     }
+    if args.only in ("all", "step", "decode") and run_d:
+        log("[bench] machine context: read-stream bandwidth and shader clock")
+        rec["context"] = machine_context(fa, dev, stream, dk.view(torch.uint8).view(-1))
     if args.only in ("all", "next"):
         rec["next"] = time_next(fa, syn, upload, dev, stream, args.steps, args.warmup,
                                 (dq, dk, dv, wd.scale, S) if run_d else None)

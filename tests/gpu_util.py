@@ -26,6 +26,16 @@ def inputs(w: syn.Workload):
     return host, f64
 
 
+def host_workers() -> int:
+    """Threads for host-side oracle work: the cores this process may use, at most 16."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def max_err(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

@@ -59,6 +59,8 @@ def test_traffic_bookkeeping(tmp_path, monkeypatch):
     write_counters(run, "prefill", "WRITE_SIZE", pk, [500.0, 700.0])
     write_counters(run, "decode", "FETCH_SIZE", dk, [8000.0] * 4)
     write_counters(run, "decode", "WRITE_SIZE", dk, [16.0] * 4)
+    write_counters(run, "prefill_c4", "FETCH_SIZE", pk, [4000.0])
+    write_counters(run, "prefill_c4", "WRITE_SIZE", pk, [800.0])
     bench.write_traffic(run)
 
     rec = json.load(open(root / "profiles" / "traffic.json"))
@@ -70,9 +72,12 @@ def test_traffic_bookkeeping(tmp_path, monkeypatch):
     assert pf["read_bytes"] == 2000.0 * 1024 * 2 and pf["write_bytes"] == 600.0 * 1024
     assert pf["bytes_per_launch"] == pf["read_bytes"] + pf["write_bytes"]
     assert dc["bytes_per_launch"] == 8000.0 * 1024 * 2 + 16.0 * 1024
+    c4 = rec["prefill_bf16_c4"]
+    assert c4["dispatches"] == 1 and c4["bytes_per_launch"] == 4000.0 * 1024 * 2 + 800.0 * 1024
     # algorithmic bytes of the two workloads: Q, K, V read and O, LSE written; K, V, q read
     assert pf["algorithmic_bytes"] == 4 * 32 * 8192 * 128 * 2 + 32 * 8192 * 4
     assert dc["algorithmic_bytes"] == 2 * 64 * 32 * 8192 * 128 * 2 + 64 * 32 * 128 * 2
+    assert c4["algorithmic_bytes"] == pf["algorithmic_bytes"]  # same tensors as c3, another query mix
 
     assert bench.traffic_from_profiles("prefill_bf16_c3") == pf["bytes_per_launch"]
     assert bench.traffic_from_profiles("decode_split_c5") == dc["bytes_per_launch"]
