@@ -36,6 +36,14 @@ def host_workers() -> int:
     return max(1, min(16, n))
 
 
+def bf16_output_floor(ref) -> float:
+    """max |ref - bf16(ref)|: the error that rounding the exact output to bf16 (round to nearest even) costs
+    by itself, the least any bf16-output kernel can reach on these rows."""
+    import torch
+    r = torch.from_numpy(np.ascontiguousarray(ref, dtype=np.float64))
+    return float((r - r.to(torch.bfloat16).to(torch.float64)).abs().max()) if r.numel() else 0.0
+
+
 def max_err(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
