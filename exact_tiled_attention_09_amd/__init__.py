@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.fa_decode_workspace_bytes.restype = sz
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp, i]
+    L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
     L.fa_decode_split.argtypes = [vp, vp, vp, i, i, i, i, f, i, vp, sz, vp, i]
     L.fa_decode_combine.argtypes = [vp, sz, vp, vp, i, i, i, i, vp, i]
     L.fa_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -91,7 +92,8 @@ def lib() -> ctypes.CDLL:
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = ctypes.c_char_p
     for name in ("fa_fwd", "fa_fwd_bf16", "fa_fwd_f32", "fa_decode", "fa_decode_split", "fa_decode_combine",
-                 "fa_decode_num_splits", "fa_bwd", "fa_fwd_split", "fa_decode_gqa", "fa_decode_gqa_num_splits"):
+                 "fa_decode_num_splits", "fa_bwd", "fa_fwd_split", "fa_decode_gqa", "fa_decode_gqa_num_splits",
+                 "fa_decode_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -216,6 +218,26 @@ def fa_decode(q, k, v, o, lse, scale: float, num_splits: int, workspace, stream=
     st = lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nkv, d, float(scale), int(num_splits),
                          _ptr(workspace), nws, _stream(stream), _dtype_code(k))
     _check(st, "fa_decode")
+
+
+# Bytes of the scratch array fa_decode_noalloc keeps per GPU (FA_NOALLOC_SCRATCH_BYTES in fa.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def fa_decode_noalloc(q, k, v, o, lse, scale: float, num_splits: int, stream=None):
+    """libfa fa_decode_noalloc: fa_decode with the split partials in the library's built-in per-GPU scratch
+    (no workspace, no device allocation).  Calls that overlap in time on one GPU race on that scratch."""
+    import torch
+    B, H, Nkv, d = k.shape
+    _check_tensor("k", k, (B, H, Nkv, d), k.dtype)
+    _check_tensor("q", q, (B, H, d), k.dtype)
+    _check_tensor("v", v, (B, H, Nkv, d), k.dtype)
+    _check_tensor("o", o, (B, H, d), k.dtype)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H), torch.float32)
+    st = lib().fa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nkv, d, float(scale),
+                                 int(num_splits), _stream(stream), _dtype_code(k))
+    _check(st, "fa_decode_noalloc")
 
 
 def fa_decode_split(q, k, v, scale: float, num_splits: int, workspace, stream=None):

@@ -183,6 +183,44 @@ int fwd_split_auto(int B, int H, int N_q, int N_kv, int num_cu) {
 
 }  // namespace
 
+// Scratch of the allocation-free decode: one copy per GPU, in the library's code object, so no call ever
+// allocates.  Host code uses only the address looked up per device below, never the array's name (on the
+// host that name is a stand-in, not a device address).
+constexpr size_t kNoAllocScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+
+// The current device's copy of `scratch`, looked up on the first call on that device with the device
+// current.  Two threads racing here look up and store the same address.
+fa_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // reported here; not left pending for the next call
+    return fail(FA_ERR_DEVICE, "fa_decode_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(FA_ERR_DEVICE, "fa_decode_noalloc: device %d beyond the %d the library tracks", dev, kMaxScratchDevices);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(FA_ERR_DEVICE, "fa_decode_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    }
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q, int N_kv,
@@ -311,6 +349,25 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
   st = fa_decode_split(q, k, v, B, H, N_kv, d, scale, S, workspace, workspace_bytes, stream, dtype);
   if (st != FA_OK) return st;
   return fa_decode_combine(workspace, workspace_bytes, o, lse, B, H, d, S, stream, dtype);
+}
+
+fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                            int N_kv, int d, float scale, int num_splits, void* stream, fa_dtype dtype) {
+  int S = 0;
+  fa_status st = check_decode_sizes(B, H, N_kv, d, num_splits, &S);
+  if (st != FA_OK) return st;
+  const size_t need = ws_bytes(B, H, d, S);
+  if (need > kNoAllocScratchBytes)
+    return fail(FA_ERR_WORKSPACE,
+                "fa_decode_noalloc: the partials need %zu bytes, the built-in scratch holds %zu (B*H*S*(d+1)*4 must "
+                "fit; call fa_decode with a workspace instead)",
+                need, kNoAllocScratchBytes);
+  const fa_status pend = take_pending("fa_decode_noalloc");
+  if (pend != FA_OK) return pend;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != FA_OK) return st;
+  return fa_decode(q, k, v, o, lse, B, H, N_kv, d, scale, S, ws, kNoAllocScratchBytes, stream, dtype);
 }
 
 int fa_fwd_split_num_splits(int B, int H, int N_q, int N_kv, int d) {

@@ -125,6 +125,29 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
                     fa_dtype dtype);
 
 /*
+ * fa_decode_noalloc -- fa_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * split partials go to a scratch array built into the library (FA_NOALLOC_SCRATCH_BYTES
+ * of device memory per GPU, held from the first call on that GPU until the process ends)
+ * instead of a caller workspace; the caller passes only inputs and outputs.  Arguments,
+ * layouts, split count and results are those of fa_decode (same kernels: bit-identical
+ * o and lse for the same num_splits).
+ *   - Calls no hipMalloc/hipFree.  The first call on a device looks up that device's
+ *     copy of the array (hipGetSymbolAddress) and keeps its address.
+ *   - FA_ERR_WORKSPACE when the partials, fa_decode_workspace_bytes(B, H, N_kv, d,
+ *     num_splits), exceed FA_NOALLOC_SCRATCH_BYTES (e.g. B*H*S*(d+1)*4 > 32 MiB); use
+ *     fa_decode with a workspace then.  Nothing is launched on any error.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *     partials: calls that overlap in time on one GPU (different streams or threads)
+ *     race and may return wrong results; issue them in one stream order.  Nothing in
+ *     the array needs to start at zero: the split kernel writes every partial (empty
+ *     key ranges included) before the combine reads it.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                            int N_kv, int d, float scale, int num_splits, void* stream, fa_dtype dtype);
+
+/*
  * The two halves of fa_decode, for callers that time or reuse them separately.
  * fa_decode_split writes only the workspace partials; fa_decode_combine reads
  * partials laid out as above (S = num_splits, which must be >= 1 here) and writes

@@ -224,3 +224,24 @@ def test_probes_reject_bad_arguments(L):
     assert L.fa_probe_clock(None, 100, 4, 10, None) == 1
     assert L.fa_probe_clock(P(0), 19, 4, 10, None) == 1
     assert L.fa_probe_clock(P(0), 20, 4, 0, None) == 1
+
+
+def test_noalloc_scratch_limit(L):
+    """fa_decode_noalloc: the scratch size in the header is the binding's, and requests whose partials do not
+    fit it (or that fa_decode rejects by size) are refused before any device call."""
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.NOALLOC_SCRATCH_BYTES
+
+    def call(B, H, N, d, S):
+        return L.fa_decode_noalloc(P(0), P(1), P(2), P(3), P(4), B, H, N, d, 0.1, S, None, 0)
+
+    # 64 x 32 heads x 64 splits x 129 floats = 67.6 MB of partials > 32 MiB
+    assert call(64, 32, 8192, 128, 64) == fa.FA_ERR_WORKSPACE
+    assert "scratch" in fa.last_error()
+    # the largest split count that fits: B*H*S*(d+1)*4 <= 32 MiB
+    assert 64 * 32 * 31 * 129 * 4 <= fa.NOALLOC_SCRATCH_BYTES < 64 * 32 * 32 * 129 * 4
+    assert call(64, 32, 8192, 128, 32) == fa.FA_ERR_WORKSPACE
+    assert call(1, 1, 8, 96, 1) == fa.FA_ERR_UNSUPPORTED
+    assert call(1, 1, 8, 64, 9) == fa.FA_ERR_INVALID_ARG
+    assert call(0, 1, 8, 64, 1) == fa.FA_ERR_INVALID_ARG
