@@ -57,13 +57,17 @@ struct BwdCfg {
   static_assert(TKV % (NT * 16) == 0 && 32 * ROWB % (NT * 16) == 0, "tile loads must divide evenly");
 };
 
-// Row swizzle (16-byte chunk XOR) for tiles that are read both as MFMA rows (32 lanes, 32 rows, one
-// logical chunk) and through ds_read_b64_tr_b16 (16 lanes, 4 consecutive rows, two adjacent chunks):
-// rows that meet in one read get chunks in distinct bank groups in both patterns.
+// Row swizzle (16-byte chunk XOR) for tiles that are read both as MFMA rows and through
+// ds_read_b64_tr_b16.  The LDS serves 64 banks of 4 bytes (256 bytes) per cycle: a ds_read_b128 in
+// passes of 16 lanes, a ds_read_b64_tr_b16 in passes of 32.  Row reads put 16 rows at one logical chunk
+// into a pass, so the XOR must be a bijection over those rows; transposing reads put 4 consecutive rows
+// times 4 consecutive chunks (one aligned group of 4) into a pass, so the 4 rows must XOR their chunks
+// into distinct groups of 4.  d = 128 (a row is exactly the 64 banks): bits 2-3 of the XOR come from
+// r % 4, bits 0-1 from r / 4 % 4.  d = 64 (two rows per 256 bytes): rows of equal parity share a bank
+// half; bit 2 from r / 2 % 2, bits 0-1 from r / 4 % 4.
 template <int D>
 __device__ __forceinline__ int swz_kv(int r) {
-  return D == 128 ? (((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1))
-                  : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // Per-lane LDS byte offsets of the two transposing reads (u = 0, 1: rows 8u + 4h + j/4 of a 16-row
