@@ -16,26 +16,25 @@ namespace fa {
 namespace {
 
 // Read of n16 16-byte words with the non-temporal policy (read once, not kept in the caches): work-group g
-// reads the 32 KB chunks g, g + G, g + 2G, ... (G groups), each as four coalesced 8 KB waves of loads in
-// flight per thread (thread t of the group reads words 512 j + t of the chunk, j = 0..3).  Each thread
-// folds what it read into one word so the loads stay live; the fold is stored per thread.
+// streams the contiguous span [g * per, (g + 1) * per) of words, per = ceil(n16 / groups), as steps of
+// four coalesced 8 KB loads in flight per group (thread t reads words 512 u + t of the step, u = 0..3),
+// then the words of the span's last partial step one at a time.  Each thread folds what it read into
+// one word so the loads stay live; the fold is stored per thread.
 __global__ __launch_bounds__(512) void read_probe_kernel(const u32x4* __restrict__ src, size_t n16,
                                                          uint32_t* __restrict__ sink) {
-  constexpr size_t kChunk = 4 * 512;  // 16-byte words per chunk
-  const size_t n_chunks = n16 / kChunk;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t beg = (size_t)blockIdx.x * per;
+  const size_t end = beg + per < n16 ? beg + per : n16;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (size_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
-    const u32x4* p = src + c * kChunk + threadIdx.x;
-    const u32x4 a = __builtin_nontemporal_load(p);
-    const u32x4 b = __builtin_nontemporal_load(p + 512);
-    const u32x4 d = __builtin_nontemporal_load(p + 1024);
-    const u32x4 e = __builtin_nontemporal_load(p + 1536);
+  size_t i = beg + threadIdx.x;
+  for (; i + 3 * 512 < end; i += 4 * 512) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + 512);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 1024);
+    const u32x4 e = __builtin_nontemporal_load(src + i + 1536);
     acc ^= (a ^ b) ^ (d ^ e);
   }
-  // the tail that does not fill a chunk
-  for (size_t i = n_chunks * kChunk + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
-       i += (size_t)gridDim.x * blockDim.x)
-    acc ^= __builtin_nontemporal_load(src + i);
+  for (; i < end; i += 512) acc ^= __builtin_nontemporal_load(src + i);
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 

@@ -20,10 +20,11 @@ extern "C" {
 #endif
 
 /*
- * Reads the `bytes` bytes at buf (device memory, 16-byte aligned; bytes >= 16, a multiple of 16 is
- * read in full) once with 16-byte non-temporal loads, `groups` work-groups of 512 threads taking
- * 32 KB chunks in turn (four coalesced loads in flight per thread).  Each thread stores a fold of what it read into sink (device memory, 4-byte
- * aligned, sink_bytes >= groups * 512 * 4), which keeps the loads from being optimised away.
+ * Reads the first bytes / 16 * 16 bytes at buf (device memory, 16-byte aligned, bytes >= 16) once with
+ * 16-byte non-temporal loads.  Each of `groups` work-groups of 512 threads streams one contiguous
+ * span of about bytes / groups bytes, four coalesced 8 KB loads in flight per step (two groups per
+ * compute unit read fastest).  Each thread stores a fold of what it read into sink (device memory,
+ * 4-byte aligned, sink_bytes >= groups * 512 * 4), so the loads cannot be optimised away.
  * Bandwidth = bytes / (the kernel's duration).
  */
 int fa_probe_read_bandwidth(const void* buf, size_t bytes, void* sink, size_t sink_bytes, int groups, void* stream);
