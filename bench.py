@@ -6,7 +6,8 @@ A step is one pass over every kernel of the path on its workload, inputs already
   * fa_fwd, bf16, causal, B=1 H=32 N=8192 d=128, scale 1/sqrt(128)   (prefill; the headline value)
   * fa_decode, bf16, B=64 H=32 N_kv=8192 d=128, 16 splits + combine   (split-KV decode)
   * fa_fwd, fp32, non-causal, B=1 H=1 N=256 d=64, scale 1/8            (fp32 path)
-W untimed warm-up steps, then K timed steps between device synchronisations.  Every launch is
+Untimed steps for 0.25 s (the clock ramps up from idle under load), then W untimed warm-up steps, then
+K timed steps between device synchronisations.  Every launch is
 bracketed by HIP events on the stream it runs on, which gives each kernel's average duration over
 the timed region.  value = prefill TFLOP/s (algorithmic flops 4*d per allowed pair / kernel time);
 the decode figures (GB/s of algorithmic bytes) sit in "decode".  "context" holds the read bandwidth of a
@@ -390,6 +391,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=None,
+                    help="seconds of untimed steps before the warm-up, so the timed steps see the clock the GPU "
+                         "holds under this load rather than its ramp from idle (default 0.25 for the full run, "
+                         "0 with --only, whose profiler runs count dispatches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "step", "prefill", "decode", "f32", "next", "prefill_c2", "prefill_c4",
                                        "backward"], default="all",
@@ -498,6 +503,19 @@ def main():
         if ev is not None:
             ev[4].record(stream)
 
+    # The shader clock ramps up from idle over the first tens of milliseconds of load (a 5-step warm-up
+    # leaves the first timed steps ~6% slower than the rest).  The step therefore runs untimed, in
+    # synchronised batches, until --settle seconds have passed, then the W warm-up steps, then the K
+    # timed steps; the record states how long and how many steps the settling took.
+    settle = args.settle if args.settle is not None else (0.25 if args.only == "all" else 0.0)
+    log(f"[bench] settle {settle} s")
+    t_settle0, n_settle = time.perf_counter(), 0
+    while time.perf_counter() - t_settle0 < settle:
+        for _ in range(5):
+            step()
+        n_settle += 5
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle0
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -538,6 +556,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": round(settle_s, 3), "steps": n_settle},
         "ms_per_step": kms(t_step, args.only in ("all", "step")),
         "higher_is_better": True,
         "scaling": "weak",
