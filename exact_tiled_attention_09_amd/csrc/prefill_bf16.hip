@@ -496,13 +496,15 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 ? 1 : 2)) void prefill_bf16_kerne
 
 // ---------------------------------------------------------------------------------------------- launch
 
+#ifndef FA_PREFILL_D64_UNIT
 int64_t prefill_bf16_grid(int B, int H, int Nq, int d, int splits) {
   const int br = 128;  // the smallest query tile of any launch (an upper bound on the grid)
   return (int64_t)B * H * ((Nq + br - 1) / br) * (splits > 0 ? splits : 1);
 }
+#endif
 
 template <int D, bool CAUSAL, bool SPLIT, bool PAGED = false, bool NT = false, int NW = 4>
-static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t s) {
   using C = Cfg<D, NW>;
   PrefillParams p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -537,6 +539,18 @@ static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef FA_PREFILL_D64_UNIT
+// The d = 64 instances are compiled in their own unit (prefill_bf16_d64.hip), with the scheduler
+// strategy that measured fastest for them; this unit only refers to them.
+extern template hipError_t launch_prefill_d<64, false, true, true, false, 4>(const PrefillArgs&, hipStream_t);
+extern template hipError_t launch_prefill_d<64, false, true, true, true, 4>(const PrefillArgs&, hipStream_t);
+extern template hipError_t launch_prefill_d<64, true, true, false, true, 4>(const PrefillArgs&, hipStream_t);
+extern template hipError_t launch_prefill_d<64, false, true, false, true, 4>(const PrefillArgs&, hipStream_t);
+extern template hipError_t launch_prefill_d<64, true, true, false, false, 4>(const PrefillArgs&, hipStream_t);
+extern template hipError_t launch_prefill_d<64, false, true, false, false, 4>(const PrefillArgs&, hipStream_t);
+extern template hipError_t launch_prefill_d<64, true, false, false, false, 4>(const PrefillArgs&, hipStream_t);
+extern template hipError_t launch_prefill_d<64, false, false, false, false, 4>(const PrefillArgs&, hipStream_t);
+
 LaunchPlan plan_prefill_bf16(int B, int H, int Nq, int d, bool causal, int splits, int num_cu) {
   LaunchPlan pl;
   // d = 128 with at least one 8-wave work-group (256 query rows) per CU: 8 waves, which share each K / V
@@ -559,24 +573,35 @@ int prefill_split_tiles(int Nkv, int S) {
 
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, hipStream_t s) {
   if (a.Nq > (a.d == 128 ? Cfg<128>::BR : Cfg<64>::BR))  // more than one query tile re-reads every page
-    return a.d == 128 ? launch_d<128, false, true, true, false>(a, s) : launch_d<64, false, true, true, false>(a, s);
-  return a.d == 128 ? launch_d<128, false, true, true, true>(a, s) : launch_d<64, false, true, true, true>(a, s);
+    return a.d == 128 ? launch_prefill_d<128, false, true, true, false>(a, s) : launch_prefill_d<64, false, true, true, false>(a, s);
+  return a.d == 128 ? launch_prefill_d<128, false, true, true, true>(a, s) : launch_prefill_d<64, false, true, true, true>(a, s);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   if (a.splits > 0) {
     if (a.Nq <= (a.d == 128 ? Cfg<128>::BR : Cfg<64>::BR)) {  // one query tile: K and V are streamed once
       if (a.d == 128)
-        return a.causal ? launch_d<128, true, true, false, true>(a, s) : launch_d<128, false, true, false, true>(a, s);
-      return a.causal ? launch_d<64, true, true, false, true>(a, s) : launch_d<64, false, true, false, true>(a, s);
+        return a.causal ? launch_prefill_d<128, true, true, false, true>(a, s) : launch_prefill_d<128, false, true, false, true>(a, s);
+      return a.causal ? launch_prefill_d<64, true, true, false, true>(a, s) : launch_prefill_d<64, false, true, false, true>(a, s);
     }
-    if (a.d == 128) return a.causal ? launch_d<128, true, true>(a, s) : launch_d<128, false, true>(a, s);
-    return a.causal ? launch_d<64, true, true>(a, s) : launch_d<64, false, true>(a, s);
+    if (a.d == 128) return a.causal ? launch_prefill_d<128, true, true>(a, s) : launch_prefill_d<128, false, true>(a, s);
+    return a.causal ? launch_prefill_d<64, true, true>(a, s) : launch_prefill_d<64, false, true>(a, s);
   }
   if (plan_prefill_bf16(a.B, a.H, a.Nq, a.d, a.causal, 0, a.num_cu).waves == 8)
-    return a.causal ? launch_d<128, true, false, false, false, 8>(a, s) : launch_d<128, false, false, false, false, 8>(a, s);
-  if (a.d == 128) return a.causal ? launch_d<128, true, false>(a, s) : launch_d<128, false, false>(a, s);
-  return a.causal ? launch_d<64, true, false>(a, s) : launch_d<64, false, false>(a, s);
+    return a.causal ? launch_prefill_d<128, true, false, false, false, 8>(a, s) : launch_prefill_d<128, false, false, false, false, 8>(a, s);
+  if (a.d == 128) return a.causal ? launch_prefill_d<128, true, false>(a, s) : launch_prefill_d<128, false, false>(a, s);
+  return a.causal ? launch_prefill_d<64, true, false>(a, s) : launch_prefill_d<64, false, false>(a, s);
 }
+
+#else
+template hipError_t launch_prefill_d<64, false, true, true, false, 4>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_prefill_d<64, false, true, true, true, 4>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_prefill_d<64, true, true, false, true, 4>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_prefill_d<64, false, true, false, true, 4>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_prefill_d<64, true, true, false, false, 4>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_prefill_d<64, false, true, false, false, 4>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_prefill_d<64, true, false, false, false, 4>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_prefill_d<64, false, false, false, false, 4>(const PrefillArgs&, hipStream_t);
+#endif
 
 }  // namespace fa
