@@ -7,7 +7,8 @@ A step is one pass over every kernel of the path on its workload, inputs already
   * fa_decode, bf16, B=64 H=32 N_kv=8192 d=128, 16 splits + combine   (split-KV decode)
   * fa_fwd, fp32, non-causal, B=1 H=1 N=256 d=64, scale 1/8            (fp32 path)
 Untimed steps for 0.25 s (the clock ramps up from idle under load), then W untimed warm-up steps, then
-K timed steps between device synchronisations.  Every launch is
+K timed steps between device synchronisations (the extra workloads in "next" and the two probes each get
+the same 0.25 s of untimed calls before their warm-up).  Every launch is
 bracketed by HIP events on the stream it runs on, which gives each kernel's average duration over
 the timed region.  value = prefill TFLOP/s (algorithmic flops 4*d per allowed pair / kernel time);
 the decode figures (GB/s of algorithmic bytes) sit in "decode".  "context" holds the read bandwidth of a
@@ -116,9 +117,20 @@ def write_traffic(run_dir: str, copy_bytes: int = 1 << 30):
     print(json.dumps(out, indent=1))
 
 
+# Seconds of untimed calls before each measurement of time_events (set by main from --settle): the GPU idles
+# while the host generates the next workload's inputs, and the shader clock ramps up again from there.
+SETTLE_S = {"value": 0.0}
+
+
 def time_events(fn, stream, steps: int, warmup: int):
-    """Average duration (ms) of fn() over `steps` calls, each bracketed by HIP events on `stream`."""
+    """Average duration (ms) of fn() over `steps` calls, each bracketed by HIP events on `stream`, after
+    SETTLE_S seconds of untimed calls in synchronised batches of five and `warmup` more calls."""
     import torch
+    t_end = time.perf_counter() + SETTLE_S["value"]
+    while time.perf_counter() < t_end:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -508,6 +520,7 @@ def main():
     # synchronised batches, until --settle seconds have passed, then the W warm-up steps, then the K
     # timed steps; the record states how long and how many steps the settling took.
     settle = args.settle if args.settle is not None else (0.25 if args.only == "all" else 0.0)
+    SETTLE_S["value"] = settle  # the same settling before each of the extra workloads and probes
     log(f"[bench] settle {settle} s")
     t_settle0, n_settle = time.perf_counter(), 0
     while time.perf_counter() - t_settle0 < settle:
