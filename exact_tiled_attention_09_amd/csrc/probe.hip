@@ -1,6 +1,6 @@
 // Measurement probes (declared in include/fa_probe.h): the read-stream bandwidth the HBM actually
 // delivers to a plain streaming kernel, and the shader clock under dense matrix-core load.  They put the
-// attention kernels' figures in context (a decode kernel is judged against what a plain read reaches, a
+// attention kernels' figures in context (a decode kernel is read against what a plain streaming read reaches, a
 // prefill kernel against the clock the chip holds under MFMA load); they are not part of the attention
 // path and share no code with it.
 #include <math.h>
