@@ -409,10 +409,11 @@ def main():
                          "0 with --only, whose profiler runs count dispatches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "step", "prefill", "decode", "f32", "next", "prefill_c2", "prefill_c4",
-                                       "backward"], default="all",
+                                       "backward", "chunked"], default="all",
                     help="launch only this part (for profiler runs): 'step' is the timed step without the extra "
                          "workloads, 'next' only the extra workloads; 'prefill_c2' / 'prefill_c4' the other two causal "
-                         "bf16 prefill workloads and 'backward' fa_bwd on the headline prefill workload, each "
+                         "bf16 prefill workloads, 'backward' fa_bwd on the headline prefill workload and 'chunked' "
+                         "fa_fwd_split on the chunked-prefill workload, each "
                          "--warmup + --steps times (a JSON line with their mean times is printed)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the step, run 5 device-to-device copies of this many bytes (calibrates "
@@ -452,8 +453,9 @@ def main():
             return torch.from_numpy(x).to(dev)
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    if args.only in ("prefill_c2", "prefill_c4", "backward"):  # one workload alone, for profiler runs
-        w = syn.WORKLOADS["c3" if args.only == "backward" else args.only[-2:]]
+    if args.only in ("prefill_c2", "prefill_c4", "backward", "chunked"):  # one workload alone, for profiler runs
+        w = (syn.NEXT_WORKLOADS["chunk"] if args.only == "chunked"
+             else syn.WORKLOADS["c3" if args.only == "backward" else args.only[-2:]])
         q, k, v = (upload(syn.make_tensor(w, t), "bf16") for t in "qkv")
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
@@ -464,6 +466,11 @@ def main():
             ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq), dtype=torch.uint8, device=dev)
             fn = lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, w.scale, True, ws, stream)  # noqa: E731
             fl = 2.5 * w.flops
+        elif args.only == "chunked":
+            S = fa.fa_fwd_split_num_splits(w.B, w.H, w.Nq, w.Nkv, w.d)
+            ws = torch.empty(fa.fa_fwd_split_workspace_bytes(w.B, w.H, w.Nq, w.d, S), dtype=torch.uint8, device=dev)
+            fn = lambda: fa.fa_fwd_split(q, k, v, o, lse, w.scale, True, S, ws, stream)  # noqa: E731
+            fl = w.flops
         else:
             fn = lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, True, stream)  # noqa: E731
             fl = w.flops

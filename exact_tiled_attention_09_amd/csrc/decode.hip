@@ -401,29 +401,43 @@ __global__ __launch_bounds__(kDecThreads) void decode_paged_kernel(PagedParams p
   }
 }
 
-// One work-group of d threads per (b, h): M = max_s lse_s, w_s = exp(lse_s - M),
-// o = sum w_s O_s / sum w_s (rounded to bf16), lse = M + ln sum w_s.
+// Per row (one (b, h), or one query row of a split prefill): M = max_s lse_s, w_s = exp(lse_s - M),
+// o = sum w_s O_s / sum w_s (rounded to bf16), lse = M + ln sum w_s.  Each thread owns four consecutive
+// d of one row (16-byte loads of the fp32 partials, an 8-byte store of the bf16 result), so a 256-thread
+// work-group covers 256 / (D / 4) rows; the loop over ranges is unrolled so several loads are in flight.
+// Per element the operations and their order are those of a plain loop over s.
+constexpr int kCombineThreads = 256;
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws_o,
-                                                           const float* __restrict__ ws_lse,
-                                                           uint16_t* __restrict__ o, float* __restrict__ lse, int S) {
-  const int bh = blockIdx.x, t = threadIdx.x;
-  const float* __restrict__ L = ws_lse + (size_t)bh * S;
-  const float* __restrict__ Os = ws_o + (size_t)bh * S * D;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float* __restrict__ ws_o,
+                                                                        const float* __restrict__ ws_lse,
+                                                                        uint16_t* __restrict__ o,
+                                                                        float* __restrict__ lse, int64_t rows, int S) {
+  constexpr int TPR = D / 4, RPW = kCombineThreads / TPR;  // threads per row, rows per work-group
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  const int d0 = 4 * (threadIdx.x % TPR);
+  if (row >= rows) return;
+  const float* __restrict__ L = ws_lse + (size_t)row * S;
+  const float* __restrict__ Os = ws_o + (size_t)row * S * D + d0;
   float M = kNegInf;
   for (int s = 0; s < S; ++s) M = fmaxf(M, L[s]);
-  float sw = 0.f, acc = 0.f;
+  float sw = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
     const float ls = L[s];
     const float wgt = (ls == kNegInf) ? 0.f : exp2_hw((ls - M) * kLog2e);
     sw += wgt;
-    acc = fmaf(wgt, Os[(size_t)s * D + t], acc);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(Os + (size_t)s * D);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, v[e], acc[e]);
   }
   // sw == 0 only when every range was empty (a paged sequence with no tokens): O = 0, LSE = -inf
-  const float r = sw > 0.f ? acc / sw : 0.f;
-  const __bf16 b = (__bf16)r;
-  o[(size_t)bh * D + t] = __builtin_bit_cast(uint16_t, b);
-  if (t == 0 && lse) lse[bh] = sw > 0.f ? M + log2_hw(sw) * kLn2 : kNegInf;
+  u32x2 out;
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    out[e] = pack_bf16x2(sw > 0.f ? acc[2 * e] / sw : 0.f, sw > 0.f ? acc[2 * e + 1] / sw : 0.f);
+  *reinterpret_cast<u32x2*>(o + (size_t)row * D + d0) = out;
+  if (d0 == 0 && lse) lse[row] = sw > 0.f ? M + log2_hw(sw) * kLn2 : kNegInf;
 }
 
 hipError_t launch_decode_split_bf16(const DecodeArgs& a, hipStream_t s) {
@@ -484,12 +498,16 @@ hipError_t launch_decode_paged_bf16(const PagedDecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_combine_bf16(const CombineArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.B * a.H));
+  const int64_t rows = (int64_t)a.B * a.H;
+  const int rpw = kCombineThreads / (a.d / 4);
+  const dim3 grid((unsigned)((rows + rpw - 1) / rpw));
   uint16_t* o = static_cast<uint16_t*>(a.o);
   if (a.d == 128)
-    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(128), 0, s, a.ws_o, a.ws_lse, o, a.lse, a.splits);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(kCombineThreads), 0, s, a.ws_o, a.ws_lse, o, a.lse,
+                       rows, a.splits);
   else
-    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(64), 0, s, a.ws_o, a.ws_lse, o, a.lse, a.splits);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(kCombineThreads), 0, s, a.ws_o, a.ws_lse, o, a.lse,
+                       rows, a.splits);
   return hipGetLastError();
 }
 
